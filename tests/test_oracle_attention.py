@@ -1,0 +1,239 @@
+"""Pins of the fp64 attention oracle (CPU only).
+
+The oracle is checked against: a pure-loop brute force, PyTorch's
+scaled_dot_product_attention in float64 with an explicit block-diagonal causal
+mask on the unpartitioned packed sequence (a library special case), closed
+forms (zero queries, document-start rows), plain causal attention for one
+document at cp=1, float64 autograd of the library formulation, central finite
+differences, and gradient identities that hold for any softmax attention.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import attention, partition
+
+
+def _case(seed, lengths, cp, rank, hq, hkv, dqk, dv, with_do=False):
+    rng = np.random.default_rng(seed)
+    total = int(sum(lengths))
+    q = rng.standard_normal((total // cp, hq, dqk))
+    k = rng.standard_normal((total, hkv, dqk))
+    v = rng.standard_normal((total, hkv, dv))
+    do = rng.standard_normal((total // cp, hq, dv)) if with_do else None
+    return q, k, v, do
+
+
+def _library_reference(q_loc, k, v, lengths, cp, rank, scale):
+    """SDPA(float64) over the unpartitioned sequence, returned for the rank's rows.
+
+    Every rank's queries are needed to rebuild the global Q; other ranks' rows
+    are filled with independent noise, which the mask keeps out of this rank's
+    outputs.
+    """
+    total = int(sum(lengths))
+    qg = partition.q_global(lengths, cp, rank)
+    kg = attention.to_global(k, lengths, cp)
+    vg = attention.to_global(v, lengths, cp)
+    q_full = np.random.default_rng(999).standard_normal((total,) + q_loc.shape[1:])
+    q_full[qg] = q_loc
+    docs = partition.doc_of(lengths)
+    idx = np.arange(total)
+    mask = (docs[:, None] == docs[None, :]) & (idx[None, :] <= idx[:, None])
+    group = q_loc.shape[1] // k.shape[1]
+    qt = torch.from_numpy(q_full).permute(1, 0, 2)
+    kt = torch.from_numpy(kg).repeat_interleave(group, dim=1).permute(1, 0, 2)
+    vt = torch.from_numpy(vg).repeat_interleave(group, dim=1).permute(1, 0, 2)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt, kt, vt, attn_mask=torch.from_numpy(mask), scale=scale)
+    return out.permute(1, 0, 2).numpy()[qg]
+
+
+@pytest.mark.parametrize("lengths,cp,rank,hq,hkv,dqk,dv", [
+    ([8, 16, 8], 2, 0, 2, 1, 8, 4),
+    ([8, 16, 8], 2, 1, 4, 2, 6, 6),
+    ([12, 24], 3, 2, 3, 3, 5, 7),
+    ([8], 4, 3, 2, 2, 4, 4),
+])
+def test_numpy_oracle_matches_brute_force(lengths, cp, rank, hq, hkv, dqk, dv):
+    q, k, v, _ = _case(1, lengths, cp, rank, hq, hkv, dqk, dv)
+    o, lse = attention.attn_fwd64(q, k, v, lengths, cp, rank)
+    ob, lseb = attention.brute_fwd(q, k, v, lengths, cp, rank)
+    assert np.max(np.abs(o - ob)) <= 1e-12
+    assert np.max(np.abs(lse - lseb)) <= 1e-12
+    rows = np.arange(q.shape[0])
+    orr, lser = attention.attn_fwd64_rows(q, k, v, lengths, cp, rank, rows)
+    assert np.max(np.abs(o - orr)) <= 1e-12
+    assert np.max(np.abs(lse - lser)) <= 1e-12
+
+
+@pytest.mark.parametrize("lengths,cp,rank,hq,hkv,dqk,dv", [
+    ([64, 128, 64], 2, 0, 4, 4, 16, 16),
+    ([64, 128, 64], 2, 1, 8, 2, 16, 8),
+    ([48, 16, 96, 32], 4, 2, 4, 1, 24, 16),
+    ([80, 240], 8, 5, 2, 2, 12, 8),
+])
+def test_oracle_matches_library_sdpa(lengths, cp, rank, hq, hkv, dqk, dv):
+    q, k, v, _ = _case(2, lengths, cp, rank, hq, hkv, dqk, dv)
+    scale = 0.37
+    o, _ = attention.attn_fwd64(q, k, v, lengths, cp, rank, scale=scale)
+    ref = _library_reference(q, k, v, lengths, cp, rank, scale)
+    assert np.max(np.abs(o - ref)) <= 1e-12
+
+
+def test_single_document_cp1_is_plain_causal_attention():
+    q, k, v, _ = _case(3, [96], 1, 0, 4, 2, 16, 16)
+    o, _ = attention.attn_fwd64(q, k, v, [96], 1, 0)
+    qt = torch.from_numpy(q).permute(1, 0, 2)
+    kt = torch.from_numpy(k).repeat_interleave(2, dim=1).permute(1, 0, 2)
+    vt = torch.from_numpy(v).repeat_interleave(2, dim=1).permute(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, is_causal=True)
+    assert np.max(np.abs(o - ref.permute(1, 0, 2).numpy())) <= 1e-12
+
+
+def test_zero_queries_give_prefix_means_and_log_counts():
+    lengths, cp, rank = [16, 32, 8], 2, 1
+    q, k, v, _ = _case(4, lengths, cp, rank, 4, 2, 8, 8)
+    q[:] = 0.0
+    o, lse = attention.attn_fwd64(q, k, v, lengths, cp, rank)
+    cu = partition.cu_seqlens(lengths)
+    docs = partition.doc_of(lengths)
+    vg = attention.to_global(v, lengths, cp)
+    for row, g in enumerate(partition.q_global(lengths, cp, rank).tolist()):
+        start = cu[int(docs[g])]
+        mean = vg[start:g + 1].mean(axis=0)              # [Hkv, dv]
+        for h in range(4):
+            assert np.allclose(o[row, h], mean[h // 2], rtol=0, atol=1e-13)
+            assert abs(lse[row, h] - math.log(g - start + 1)) <= 1e-13
+
+
+def test_document_start_rows_copy_v_exactly():
+    lengths, cp = [16, 32, 8], 2
+    q, k, v, _ = _case(5, lengths, cp, 0, 4, 4, 8, 8)
+    o, lse = attention.attn_fwd64(q, k, v, lengths, cp, 0)
+    cu = partition.cu_seqlens(lengths)
+    qg = partition.q_global(lengths, cp, 0).tolist()
+    vg = attention.to_global(v, lengths, cp)
+    for start in cu[:-1]:
+        row = qg.index(start)
+        assert np.array_equal(o[row], vg[start])
+
+
+def test_eod_isolation_and_causality():
+    """Changing another document's K/V, or a later key, leaves a row unchanged."""
+    lengths, cp, rank = [16, 32, 16], 2, 0
+    q, k, v, _ = _case(6, lengths, cp, rank, 2, 2, 8, 8)
+    o, _ = attention.attn_fwd64(q, k, v, lengths, cp, rank)
+    rows = partition.kv_row(lengths, cp)
+    k2, v2 = k.copy(), v.copy()
+    k2[rows[:16]] += 5.0          # document 0's keys
+    v2[rows[:16]] -= 3.0
+    o2, _ = attention.attn_fwd64(q, k2, v2, lengths, cp, rank)
+    qg = partition.q_global(lengths, cp, rank)
+    other = qg >= 16
+    assert np.array_equal(o[other], o2[other])
+    assert not np.allclose(o[~other], o2[~other])
+    k3 = k.copy()
+    k3[rows[40:48]] += 7.0        # keys 40..47 of document 1
+    o3, _ = attention.attn_fwd64(q, k3, v, lengths, cp, rank)
+    before = qg < 40
+    assert np.array_equal(o[before], o3[before])
+
+
+def _library_grads(q_loc, k, v, do, lengths, cp, rank, scale):
+    total = int(sum(lengths))
+    qg = partition.q_global(lengths, cp, rank)
+    rows = partition.kv_row(lengths, cp)
+    docs = partition.doc_of(lengths)
+    idx = np.arange(total)
+    mask = torch.from_numpy((docs[:, None] == docs[None, :]) & (idx[None, :] <= idx[:, None]))
+    group = q_loc.shape[1] // k.shape[1]
+    q_full = np.zeros((total,) + q_loc.shape[1:])
+    q_full[qg] = q_loc
+    qt = torch.from_numpy(q_full).requires_grad_()
+    kt = torch.from_numpy(k[rows]).requires_grad_()
+    vt = torch.from_numpy(v[rows]).requires_grad_()
+    out = torch.nn.functional.scaled_dot_product_attention(
+        qt.permute(1, 0, 2), kt.repeat_interleave(group, dim=1).permute(1, 0, 2),
+        vt.repeat_interleave(group, dim=1).permute(1, 0, 2), attn_mask=mask, scale=scale)
+    out = out.permute(1, 0, 2)[torch.from_numpy(qg.astype(np.int64))]
+    (out * torch.from_numpy(do)).sum().backward()
+    dq = qt.grad.numpy()[qg]
+    dk = np.zeros_like(k)
+    dv = np.zeros_like(v)
+    dk[rows] = kt.grad.numpy()
+    dv[rows] = vt.grad.numpy()
+    return dq, dk, dv
+
+
+@pytest.mark.parametrize("lengths,cp,rank,hq,hkv,dqk,dv", [
+    ([32, 64, 32], 2, 0, 4, 2, 16, 8),
+    ([32, 64, 32], 2, 1, 4, 4, 8, 16),
+    ([48, 16, 96], 4, 3, 6, 2, 12, 8),
+])
+def test_backward_matches_library_autograd(lengths, cp, rank, hq, hkv, dqk, dv):
+    q, k, v, do = _case(7, lengths, cp, rank, hq, hkv, dqk, dv, with_do=True)
+    scale = 0.29
+    dq, dk, dvv = attention.attn_bwd64(q, k, v, do, lengths, cp, rank, scale=scale)
+    rq, rk, rv = _library_grads(q, k, v, do, lengths, cp, rank, scale)
+    for a, b in ((dq, rq), (dk, rk), (dvv, rv)):
+        assert np.max(np.abs(a - b)) <= 1e-11
+
+
+def test_backward_finite_differences():
+    lengths, cp, rank = [16, 32], 2, 1
+    q, k, v, do = _case(8, lengths, cp, rank, 4, 2, 8, 8, with_do=True)
+    dq, dk, dv = attention.attn_bwd64(q, k, v, do, lengths, cp, rank)
+
+    def loss(qq, kk, vv):
+        return float((attention.attn_fwd64(qq, kk, vv, lengths, cp, rank)[0] * do).sum())
+
+    eps = 1e-6
+    rows = partition.kv_row(lengths, cp)
+    for arr, grad, idx in ((q, dq, (3, 1, 2)), (q, dq, (20, 3, 7)),
+                           (k, dk, (int(rows[17]), 1, 4)), (v, dv, (int(rows[9]), 0, 5))):
+        plus = arr.copy(); plus[idx] += eps
+        minus = arr.copy(); minus[idx] -= eps
+        args_p = [plus if arr is x else x for x in (q, k, v)]
+        args_m = [minus if arr is x else x for x in (q, k, v)]
+        fd = (loss(*args_p) - loss(*args_m)) / (2 * eps)
+        assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd))
+
+
+def test_backward_identities():
+    lengths, cp, rank = [24, 48, 24], 3, 1
+    hq, hkv = 6, 2
+    q, k, v, do = _case(9, lengths, cp, rank, hq, hkv, 8, 8, with_do=True)
+    dq, dk, dv = attention.attn_bwd64(q, k, v, do, lengths, cp, rank)
+    group = hq // hkv
+    # rows of P sum to one: the keys' dV add up to the rows' dO, per kv head
+    for hk in range(hkv):
+        assert np.allclose(dv[:, hk].sum(0), do[:, hk * group:(hk + 1) * group].sum((0, 1)), atol=1e-12)
+        # rows of dS sum to zero, so the keys' dK add up to zero
+        assert np.allclose(dk[:, hk].sum(0), 0.0, atol=1e-12)
+    # keys no local query sees get exact zeros: offsets >= (2cp-r)*c in each document
+    cu = partition.cu_seqlens(lengths)
+    rows = partition.kv_row(lengths, cp)
+    unseen = []
+    for i, length in enumerate(lengths):
+        c = length // (2 * cp)
+        unseen.extend(range(cu[i] + (2 * cp - rank) * c, cu[i + 1]))
+    assert unseen
+    assert np.all(dk[rows[unseen]] == 0.0) and np.all(dv[rows[unseen]] == 0.0)
+    # constant keys give uniform weights and a zero query gradient
+    k_const = np.broadcast_to(k[:1], k.shape).copy()
+    dq0, _, _ = attention.attn_bwd64(q, k_const, v, do, lengths, cp, rank)
+    assert np.max(np.abs(dq0)) <= 1e-12
+
+
+def test_workload_shapes_tiny_runs():
+    w = workloads.BY_NAME["tiny"]
+    b = workloads.make_batch(w)
+    q = b.q.double().numpy()
+    rows = np.arange(0, q.shape[0], 37)
+    o, lse = attention.attn_fwd64_rows(q, b.k.double().numpy(), b.v.double().numpy(),
+                                       b.lengths, w.cp, w.rank, rows)
+    assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))

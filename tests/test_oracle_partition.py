@@ -1,0 +1,151 @@
+"""Pins of the oracle's partition and metadata (CPU only).
+
+Each test checks the oracle against something other than itself: a
+hand-derived fixture, a closed form, or a brute-force enumeration.
+"""
+import numpy as np
+import pytest
+
+import workloads
+from golden_io import read_records, runs_to_positions
+from oracle import metadata, partition
+
+
+def test_tiny_partition_matches_hand_derivation():
+    g = read_records("partition_tiny.txt")
+    lengths = g["lengths"][0]
+    cp = g["cp"][0][0]
+    assert partition.q_global(lengths, cp, 0).tolist() == runs_to_positions(g["runs0"][0])
+    assert partition.q_global(lengths, cp, 1).tolist() == runs_to_positions(g["runs1"][0])
+    rows = partition.kv_row(lengths, cp)
+    for tok, row in g["kv_row"][0]:
+        assert int(rows[tok]) == row, tok
+    for r in range(cp):
+        assert partition.visible_count(lengths, cp, r) == g["pairs"][0][0]
+
+
+@pytest.mark.parametrize("cp", [1, 2, 3, 4, 8])
+def test_partition_invariants_random(cp):
+    rng = np.random.default_rng(100 + cp)
+    lengths = workloads.random_lengths(rng, 7, cp, 9)
+    total = int(lengths.sum())
+    cu = partition.cu_seqlens(lengths)
+    allq = np.concatenate([partition.q_global(lengths, cp, r) for r in range(cp)])
+    # the ranks' query maps partition [0, T)
+    assert sorted(allq.tolist()) == list(range(total))
+    # kv_row is the inverse of the gathered (rank-major) order
+    rows = partition.kv_row(lengths, cp)
+    assert sorted(rows.tolist()) == list(range(total))
+    assert np.array_equal(rows[allq], np.arange(total))
+    # symmetric ownership: within each document rank r holds exactly chunks r and 2cp-1-r
+    for r in range(cp):
+        qg = partition.q_global(lengths, cp, r)
+        for i, length in enumerate(lengths.tolist()):
+            c = length // (2 * cp)
+            mine = [g for g in qg.tolist() if cu[i] <= g < cu[i + 1]]
+            assert sorted({(g - cu[i]) // c for g in mine}) == sorted({r, 2 * cp - 1 - r})
+            assert len(mine) == 2 * c
+    # chunk_off is the gathered row of every chunk's first token, and chunks are contiguous there
+    offs = partition.chunk_off(lengths, cp)
+    for i, length in enumerate(lengths.tolist()):
+        c = length // (2 * cp)
+        for k in range(2 * cp):
+            start = cu[i] + k * c
+            assert list(rows[start:start + c]) == list(range(offs[i * 2 * cp + k], offs[i * 2 * cp + k] + c))
+
+
+@pytest.mark.parametrize("cp", [1, 2, 4, 8])
+def test_load_balance_closed_form(cp):
+    rng = np.random.default_rng(7 * cp)
+    lengths = workloads.random_lengths(rng, 5, cp, 12)
+    closed = metadata.useful_pairs_closed_form(lengths, cp)
+    for r in range(cp):
+        assert partition.visible_count(lengths, cp, r) == closed
+
+
+def test_partition_rejects_bad_input():
+    with pytest.raises(partition.PartitionError):
+        partition.q_global([6, 8], 2, 0)       # 6 % 4 != 0
+    with pytest.raises(partition.PartitionError):
+        partition.q_global([8], 2, 2)          # rank >= cp
+    with pytest.raises(partition.PartitionError):
+        partition.q_global([], 1, 0)
+    with pytest.raises(partition.PartitionError):
+        partition.q_global([0, 4], 1, 0)
+
+
+def test_small_tiles_match_hand_derivation():
+    g = read_records("tiles_small.txt")
+    lengths, cp, rank, bt, bn = [8, 16], 2, 1, 2, 4
+    tt = metadata.tiles(lengths, cp, rank, bt, bn)
+    assert tt.tolist() == g["tile"]
+    assert metadata.order(tt).tolist() == g["order"][0]
+    assert metadata.kvtiles(lengths, cp, rank, bt, bn).tolist() == g["kvtile"]
+
+
+def _visible_pairs(lengths, cp, rank):
+    """Brute force: all (local row, global key) pairs the mask leaves open."""
+    cu = partition.cu_seqlens(lengths)
+    docs = partition.doc_of(lengths)
+    out = set()
+    for row, g in enumerate(partition.q_global(lengths, cp, rank).tolist()):
+        for key in range(cu[int(docs[g])], g + 1):
+            out.add((row, key))
+    return out
+
+
+@pytest.mark.parametrize("lengths,cp", [([8, 16, 8, 24], 1), ([8, 16, 8, 24], 2), ([8, 16, 8, 24], 4),
+                                        ([24, 8], 2), ([16], 4)])
+@pytest.mark.parametrize("bt,bn", [(1, 1), (2, 3), (3, 2), (4, 8), (8, 4)])
+def test_tiles_cover_visible_pairs_exactly(lengths, cp, bt, bn):
+    for rank in range(cp):
+        want = _visible_pairs(lengths, cp, rank)
+        tt = metadata.tiles(lengths, cp, rank, bt, bn)
+        seen = []
+        for q0, qg0, nr, doc, slot, kv0, n_kv, n_full in tt.tolist():
+            assert 1 <= nr <= bt
+            for j in range(n_kv):
+                keys = range(kv0 + j * bn, kv0 + min((j + 1) * bn, qg0 + nr - kv0))
+                pairs = [(q0 + o, key) for o in range(nr) for key in keys if key <= qg0 + o]
+                assert pairs, "a visited KV tile must hold a visible pair"
+                if j < n_full:
+                    assert len(pairs) == nr * len(keys), "a full tile needs no mask"
+                seen.extend(pairs)
+        assert len(seen) == len(set(seen)) == len(want)
+        assert set(seen) == want
+        order = metadata.order(tt)
+        assert sorted(order.tolist()) == list(range(tt.shape[0]))
+        n_kv = tt[order, 6]
+        assert all(n_kv[:-1] >= n_kv[1:])
+        # backward tiles: each visible pair covered once by (kv tile, q tile in [begin, end))
+        seen_b = []
+        for doc, ks, nk, qb, qe, *_ in metadata.kvtiles(lengths, cp, rank, bt, bn).tolist():
+            for t in range(qb, qe):
+                q0, qg0, nr = tt[t, 0], tt[t, 1], tt[t, 2]
+                assert tt[t, 3] == doc
+                seen_b.extend((q0 + o, key) for o in range(nr) for key in range(ks, ks + nk)
+                              if key <= qg0 + o)
+        assert len(seen_b) == len(set(seen_b)) == len(want)
+        assert set(seen_b) == want
+
+
+def test_kvtiles_skip_only_unseen_keys():
+    lengths, cp = [16, 32, 8], 2
+    for rank in range(cp):
+        tt = metadata.tiles(lengths, cp, rank, 2, 4)
+        kt = metadata.kvtiles(lengths, cp, rank, 2, 4)
+        keys_seen = {key for _, key in _visible_pairs(lengths, cp, rank)}
+        covered = {key for doc, ks, nk, *_ in kt.tolist() for key in range(ks, ks + nk)}
+        assert covered == keys_seen
+        # the first q tile listed for a kv tile sees its first key, the one before it does not
+        for doc, ks, nk, qb, qe, *_ in kt.tolist():
+            assert tt[qb, 1] + tt[qb, 2] - 1 >= ks
+            if qb > 0 and tt[qb - 1, 3] == doc:
+                assert tt[qb - 1, 1] + tt[qb - 1, 2] - 1 < ks
+
+
+@pytest.mark.parametrize("w", workloads.WORKLOADS, ids=lambda w: w.name)
+def test_workload_lengths_are_valid(w):
+    lengths = workloads.draw_lengths(w, np.random.default_rng(w.index))
+    assert int(lengths.sum()) == w.total
+    assert all(int(x) % (2 * w.cp) == 0 and int(x) > 0 for x in lengths)
