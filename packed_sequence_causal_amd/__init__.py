@@ -1,0 +1,261 @@
+"""Python binding of libthdattn: causal + EOD-reset attention over THD-packed
+sequences for one context-parallel rank, on AMD MI355X (gfx950).
+
+This module only marshals arguments: every step of the computation runs in
+the C-ABI library (host planner and HIP kernels). PyTorch supplies device
+memory and the stream. All functions are keyword-only, so that a change of the
+argument list cannot silently shift positional arguments.
+
+The library must have been built in-tree (``python -m
+packed_sequence_causal_amd.build`` or ``__graft_entry__.build()``); importing
+this package raises if it is missing. There is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libthdattn.so")
+
+THD_OK = 0
+STATUS_NAMES = {
+    -1: "THD_EINVAL", -2: "THD_ENOTDIV", -3: "THD_ERANGE", -4: "THD_EALIGN",
+    -5: "THD_EMISMATCH", -6: "THD_EHIP", -7: "THD_ENOMEM", -8: "THD_EUNSUPPORTED",
+}
+FIELDS = {"q_global": 0, "kv_row": 1, "chunk_off": 2, "tiles": 3, "order": 4, "kvtiles": 5}
+META_VERSION = 1
+
+
+class ThdError(RuntimeError):
+    """A negative status returned by the library, with its message."""
+
+    def __init__(self, code: int, message: str):
+        super().__init__(f"{STATUS_NAMES.get(code, code)}: {message}")
+        self.code = code
+        self.status = STATUS_NAMES.get(code, str(code))
+
+
+class _Info(ctypes.Structure):
+    _fields_ = [
+        ("total_tokens", ctypes.c_int64), ("local_tokens", ctypes.c_int64),
+        ("n_tiles", ctypes.c_int64), ("n_kvtiles", ctypes.c_int64),
+        ("useful_pairs", ctypes.c_int64), ("max_kv_tiles", ctypes.c_int64),
+        ("n_docs", ctypes.c_int32), ("cp", ctypes.c_int32), ("rank", ctypes.c_int32),
+        ("block_t", ctypes.c_int32), ("block_n", ctypes.c_int32), ("version", ctypes.c_int32),
+        ("device", ctypes.c_int32), ("cache_hit", ctypes.c_int32),
+    ]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it first with "
+            "`python -m packed_sequence_causal_amd.build` (no fallback path exists)")
+    lib = ctypes.CDLL(LIB_PATH)
+    i32, i64, p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+    pi32 = ctypes.POINTER(ctypes.c_int32)
+    pi64 = ctypes.POINTER(ctypes.c_int64)
+    sigs = {
+        "thd_last_error": (ctypes.c_char_p, []),
+        "thd_plan_partition": (ctypes.c_int, [pi32, i32, i32, i32, pi64, pi64, pi32, pi32, pi32]),
+        "thd_build_metadata": (ctypes.c_int, [pi32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(p)]),
+        "thd_meta_info": (ctypes.c_int, [p, ctypes.POINTER(_Info)]),
+        "thd_meta_copy": (ctypes.c_int, [p, i32, pi32, i64]),
+        "thd_meta_release": (None, [p]),
+        "thd_cache_stats": (ctypes.c_int, [pi64, pi64, pi64, pi64]),
+        "thd_cache_clear": (ctypes.c_int, []),
+        "thd_preferred_tiles": (ctypes.c_int, [i32, i32, i32, i32, pi32, pi32]),
+        "thd_attn_fwd": (ctypes.c_int, [p, p, p, p, p, p, i32, i32, i32, i32, ctypes.c_float, p]),
+        "thd_attn_bwd_workspace": (ctypes.c_int, [p, i32, pi64]),
+        "thd_attn_bwd": (ctypes.c_int, [p, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
+                                        ctypes.c_float, p, i64, p]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+_lib = _load()
+EXPORTS = ("thd_last_error", "thd_plan_partition", "thd_build_metadata", "thd_meta_info",
+           "thd_meta_copy", "thd_meta_release", "thd_cache_stats", "thd_cache_clear",
+           "thd_preferred_tiles", "thd_attn_fwd", "thd_attn_bwd_workspace", "thd_attn_bwd")
+
+
+def _check(code: int):
+    if code != THD_OK:
+        raise ThdError(code, _lib.thd_last_error().decode(errors="replace"))
+
+
+def _lengths(seqlens) -> np.ndarray:
+    arr = np.ascontiguousarray(np.asarray(seqlens).reshape(-1))
+    if arr.size and not np.issubdtype(arr.dtype, np.integer):
+        raise TypeError("seqlens must be integers")
+    if arr.size and (arr.min() < np.iinfo(np.int32).min or arr.max() > np.iinfo(np.int32).max):
+        raise ThdError(-3, "a length does not fit int32")
+    return np.ascontiguousarray(arr, dtype=np.int32)
+
+
+def _ptr32(arr: np.ndarray):
+    return arr.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)) if arr is not None else None
+
+
+def plan_partition(*, seqlens, cp: int, rank: int) -> dict:
+    """Per-rank partition maps (host numpy int32): q_global, kv_row, chunk_off."""
+    lens = _lengths(seqlens)
+    total, local = ctypes.c_int64(), ctypes.c_int64()
+    _check(_lib.thd_plan_partition(_ptr32(lens), len(lens), cp, rank, ctypes.byref(total),
+                                   ctypes.byref(local), None, None, None))
+    q_global = np.empty(local.value, np.int32)
+    kv_row = np.empty(total.value, np.int32)
+    chunk_off = np.empty(len(lens) * 2 * cp, np.int32)
+    _check(_lib.thd_plan_partition(_ptr32(lens), len(lens), cp, rank, None, None,
+                                   _ptr32(q_global), _ptr32(kv_row), _ptr32(chunk_off)))
+    return {"total": total.value, "local": local.value, "q_global": q_global,
+            "kv_row": kv_row, "chunk_off": chunk_off}
+
+
+class Meta:
+    """One reference to a cached metadata object; released when dropped."""
+
+    def __init__(self, handle):
+        self._h = handle
+
+    @property
+    def handle(self):
+        return self._h
+
+    def info(self) -> dict:
+        inf = _Info()
+        _check(_lib.thd_meta_info(self._h, ctypes.byref(inf)))
+        return {name: getattr(inf, name) for name, _ in _Info._fields_}
+
+    def field(self, name: str) -> np.ndarray:
+        inf = self.info()
+        n = {"q_global": inf["local_tokens"], "kv_row": inf["total_tokens"],
+             "chunk_off": inf["n_docs"] * 2 * inf["cp"], "tiles": inf["n_tiles"] * 8,
+             "order": inf["n_tiles"], "kvtiles": inf["n_kvtiles"] * 8}[name]
+        out = np.empty(n, np.int32)
+        _check(_lib.thd_meta_copy(self._h, FIELDS[name], _ptr32(out), n))
+        if name in ("tiles", "kvtiles"):
+            out = out.reshape(-1, 8)
+        return out
+
+    def release(self):
+        if self._h is not None:
+            _lib.thd_meta_release(self._h)
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.release()
+        except Exception:
+            pass
+
+
+def build_metadata(*, seqlens, cp: int, rank: int, block_t: int, block_n: int,
+                   device: int = -1) -> Meta:
+    """Build or fetch cached metadata; device >= 0 also uploads it there."""
+    lens = _lengths(seqlens)
+    h = ctypes.c_void_p()
+    _check(_lib.thd_build_metadata(_ptr32(lens), len(lens), cp, rank, block_t, block_n, device,
+                                   ctypes.byref(h)))
+    return Meta(h)
+
+
+def preferred_tiles(*, hq: int, hkv: int, d_qk: int, d_v: int) -> tuple[int, int]:
+    bt, bn = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.thd_preferred_tiles(hq, hkv, d_qk, d_v, ctypes.byref(bt), ctypes.byref(bn)))
+    return bt.value, bn.value
+
+
+def cache_stats() -> dict:
+    vals = [ctypes.c_int64() for _ in range(4)]
+    _check(_lib.thd_cache_stats(*[ctypes.byref(v) for v in vals]))
+    return dict(zip(("hits", "misses", "uploads", "entries"), (v.value for v in vals)))
+
+
+def cache_clear():
+    _check(_lib.thd_cache_clear())
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream_handle(stream, device):
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def device_metadata(*, seqlens, cp: int, rank: int, hq: int, hkv: int, d_qk: int, d_v: int,
+                    device: int) -> Meta:
+    bt, bn = preferred_tiles(hq=hq, hkv=hkv, d_qk=d_qk, d_v=d_v)
+    return build_metadata(seqlens=seqlens, cp=cp, rank=rank, block_t=bt, block_n=bn, device=device)
+
+
+def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=None, lse=None,
+             stream=None, meta: Meta | None = None):
+    """Forward attention for one rank. Returns (o bf16 [T_loc,Hq,dv], lse fp32 [T_loc,Hq]).
+
+    q [T_loc, Hq, dqk], k [T, Hkv, dqk], v [T, Hkv, dv]: bf16 CUDA tensors,
+    k/v already gathered rank-major. softmax_scale defaults to 1/sqrt(dqk).
+    """
+    torch = _torch()
+    hq, hkv, d_qk, d_v = q.shape[1], k.shape[1], q.shape[2], v.shape[2]
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 3:
+            raise ThdError(-1, f"{name} must be a contiguous 3-d bf16 device tensor")
+    device = q.device.index
+    if meta is None:
+        meta = device_metadata(seqlens=seqlens, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=d_qk,
+                               d_v=d_v, device=device)
+    inf = meta.info()
+    if q.shape[0] != inf["local_tokens"] or k.shape[0] != inf["total_tokens"] \
+            or v.shape[0] != inf["total_tokens"]:
+        raise ThdError(-5, "token counts do not match the lengths")
+    if out is None:
+        out = torch.empty((q.shape[0], hq, d_v), dtype=torch.bfloat16, device=q.device)
+    if lse is None:
+        lse = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(d_qk) if softmax_scale is None else float(softmax_scale)
+    _check(_lib.thd_attn_fwd(meta.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             out.data_ptr(), lse.data_ptr(), hq, hkv, d_qk, d_v, scale,
+                             _stream_handle(stream, q.device)))
+    return out, lse
+
+
+def attn_bwd(*, q, k, v, o, lse, d_o, seqlens, cp: int, rank: int, softmax_scale=None,
+             stream=None, meta: Meta | None = None, workspace=None):
+    """Backward for one rank. Returns (dq fp32, dk fp32, dv fp32); dk/dv are
+    this rank's partial sums in the gathered layout (zeros for unseen keys)."""
+    torch = _torch()
+    hq, hkv, d_qk, d_v = q.shape[1], k.shape[1], q.shape[2], v.shape[2]
+    device = q.device.index
+    if meta is None:
+        meta = device_metadata(seqlens=seqlens, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=d_qk,
+                               d_v=d_v, device=device)
+    inf = meta.info()
+    if q.shape[0] != inf["local_tokens"] or k.shape[0] != inf["total_tokens"]:
+        raise ThdError(-5, "token counts do not match the lengths")
+    need = ctypes.c_int64()
+    _check(_lib.thd_attn_bwd_workspace(meta.handle, hq, ctypes.byref(need)))
+    if workspace is None:
+        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
+    scale = 1.0 / math.sqrt(d_qk) if softmax_scale is None else float(softmax_scale)
+    _check(_lib.thd_attn_bwd(meta.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                             lse.data_ptr(), d_o.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                             dv.data_ptr(), hq, hkv, d_qk, d_v, scale, workspace.data_ptr(),
+                             workspace.numel(), _stream_handle(stream, q.device)))
+    return dq, dk, dv

@@ -1,0 +1,116 @@
+// Internal declarations shared by the host planner, the cache, the C ABI and
+// the kernel launchers. Not part of the public interface.
+#pragma once
+
+#include <cstdint>
+#include <memory>
+#include <string>
+#include <vector>
+
+#include "thdattn.h"
+
+namespace thd {
+
+// Error carrying a thd_status code; converted to a return value at the ABI.
+struct Error {
+  int code;
+  std::string msg;
+};
+
+[[noreturn]] void fail(int code, const std::string& msg);
+
+// Host-side plan and tile tables for one (lengths, cp, rank, block_t, block_n).
+// Field meanings are documented with THD_FIELD_* in thdattn.h.
+struct Plan {
+  std::vector<int32_t> seqlens;
+  int32_t cp = 1, rank = 0, block_t = 1, block_n = 1;
+  int64_t total = 0, local = 0, useful_pairs = 0, max_kv_tiles = 0;
+  std::vector<int32_t> q_global, kv_row, chunk_off, tiles, order, kvtiles;
+};
+
+// Checks lengths/cp/rank; throws Error. Returns T.
+int64_t validate_partition(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank);
+
+// Fills q_global / kv_row / chunk_off (any may be null) for validated input.
+void plan_partition(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank,
+                    int32_t* q_global, int32_t* kv_row, int32_t* chunk_off);
+
+// Builds the full plan (partition maps + tile tables).
+std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t cp,
+                                 int32_t rank, int32_t block_t, int32_t block_n);
+
+// Device copies of the arrays the kernels read.
+struct DeviceMeta {
+  int device = -1;
+  void* base = nullptr;          // one allocation holding every array
+  const int32_t* kv_row = nullptr;
+  const int32_t* tiles = nullptr;
+  const int32_t* order = nullptr;
+  const int32_t* kvtiles = nullptr;
+  const int32_t* q_global = nullptr;
+};
+
+struct MetaEntry {
+  std::unique_ptr<Plan> plan;
+  DeviceMeta dev;
+  ~MetaEntry();
+};
+
+}  // namespace thd
+
+// The opaque handle handed out at the ABI: one reference to a cache entry.
+struct thd_meta {
+  std::shared_ptr<thd::MetaEntry> entry;
+  bool cache_hit = false;
+};
+
+namespace thd {
+
+// Fixed kernel geometry: 4 waves of 64 lanes, 32 query rows per wave, and
+// 64-key KV tiles.
+constexpr int kWaves = 4;
+constexpr int kRowsPerWg = 128;
+constexpr int kBlockN = 64;
+
+struct FwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  const int32_t* tiles;
+  const int32_t* order;
+  const int32_t* kv_row;
+  int32_t n_tiles, hq, hkv, group, block_t;
+  int64_t total;
+  float scale_log2;   // softmax_scale * log2(e)
+};
+
+// Kernel launchers (defined in the .hip files). Return a hipError_t value.
+int launch_fwd(const FwdParams& p, int d_qk, int d_v, void* stream);
+
+struct BwdParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* o;
+  const float* lse;
+  const void* d_o;
+  float* dq;
+  float* dk;
+  float* dv;
+  float* delta;       // workspace [T_local, Hq]
+  const int32_t* tiles;
+  const int32_t* kvtiles;
+  const int32_t* kv_row;
+  int32_t n_tiles, n_kvtiles, hq, hkv, group, block_t;
+  int64_t total, local;
+  float scale;        // softmax_scale
+  float scale_log2;   // softmax_scale * log2(e)
+};
+
+int launch_bwd(const BwdParams& p, int d_qk, int d_v, void* stream);
+bool bwd_supported(int d_qk, int d_v);
+bool fwd_supported(int d_qk, int d_v);
+
+}  // namespace thd

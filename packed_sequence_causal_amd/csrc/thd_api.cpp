@@ -1,0 +1,434 @@
+// The C ABI: argument checks, the metadata cache, and kernel launches.
+//
+// Metadata is cached because it depends only on the packed lengths, cp, rank
+// and tile sizes, which repeat from step to step ("kvallgather cp thd load
+// balance", Ascend/MindSpeed, "What this PR does / why we need it?": metadata
+// caching to avoid repeated calculations). The key holds every input that
+// changes the arrays (the full length list, not just T or the document
+// count), plus the contract version and the device of the uploaded copy.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstring>
+#include <list>
+#include <mutex>
+#include <new>
+#include <string>
+#include <unordered_map>
+
+#include "internal.h"
+
+namespace thd {
+namespace {
+
+thread_local std::string g_last_error;
+
+template <class F>
+int guarded(F&& body) {
+  try {
+    body();
+    return THD_OK;
+  } catch (const Error& e) {
+    g_last_error = e.msg;
+    return e.code;
+  } catch (const std::bad_alloc&) {
+    g_last_error = "host allocation failed";
+    return THD_ENOMEM;
+  } catch (...) {
+    g_last_error = "unexpected internal error";
+    return THD_EINVAL;
+  }
+}
+
+void check_hip(hipError_t err, const char* what) {
+  if (err != hipSuccess)
+    fail(err == hipErrorOutOfMemory ? THD_ENOMEM : THD_EHIP,
+         std::string(what) + ": " + hipGetErrorString(err));
+}
+
+// Restores the caller's current device when it goes out of scope.
+struct DeviceScope {
+  int saved = -1;
+  explicit DeviceScope(int device) {
+    check_hip(hipGetDevice(&saved), "hipGetDevice");
+    if (saved != device) check_hip(hipSetDevice(device), "hipSetDevice");
+  }
+  ~DeviceScope() {
+    int now = -1;
+    if (hipGetDevice(&now) == hipSuccess && now != saved && saved >= 0) (void)hipSetDevice(saved);
+  }
+};
+
+void upload(MetaEntry& e, int device) {
+  const Plan& p = *e.plan;
+  DeviceScope scope(device);
+  const std::vector<int32_t>* parts[5] = {&p.kv_row, &p.tiles, &p.order, &p.kvtiles, &p.q_global};
+  size_t offs[5];
+  size_t bytes = 0;
+  for (int i = 0; i < 5; ++i) {
+    offs[i] = bytes;
+    bytes += (parts[i]->size() * sizeof(int32_t) + 255) / 256 * 256;
+  }
+  void* base = nullptr;
+  check_hip(hipMalloc(&base, bytes == 0 ? 256 : bytes), "hipMalloc(metadata)");
+  std::vector<char> staging(bytes);
+  for (int i = 0; i < 5; ++i)
+    if (!parts[i]->empty())
+      std::memcpy(staging.data() + offs[i], parts[i]->data(), parts[i]->size() * sizeof(int32_t));
+  const hipError_t err = hipMemcpy(base, staging.data(), bytes, hipMemcpyHostToDevice);
+  if (err != hipSuccess) {
+    (void)hipFree(base);
+    check_hip(err, "hipMemcpy(metadata)");
+  }
+  char* b = static_cast<char*>(base);
+  e.dev.device = device;
+  e.dev.base = base;
+  e.dev.kv_row = reinterpret_cast<const int32_t*>(b + offs[0]);
+  e.dev.tiles = reinterpret_cast<const int32_t*>(b + offs[1]);
+  e.dev.order = reinterpret_cast<const int32_t*>(b + offs[2]);
+  e.dev.kvtiles = reinterpret_cast<const int32_t*>(b + offs[3]);
+  e.dev.q_global = reinterpret_cast<const int32_t*>(b + offs[4]);
+}
+
+// Least-recently-used cache of metadata entries. Entries still referenced by a
+// caller's handle outlive their eviction. The cache object is never destroyed,
+// so no device memory is freed after the HIP runtime has shut down.
+struct Cache {
+  std::mutex mu;
+  std::unordered_map<std::string, std::shared_ptr<MetaEntry>> map;
+  std::list<std::string> lru;  // front: most recently used
+  std::unordered_map<std::string, std::list<std::string>::iterator> where;
+  int64_t hits = 0, misses = 0, uploads = 0;
+  static constexpr size_t kCapacity = 64;
+};
+
+Cache& cache() {
+  static Cache* c = new Cache;
+  return *c;
+}
+
+std::string make_key(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank,
+                     int32_t block_t, int32_t block_n, int32_t device) {
+  const int32_t head[7] = {THD_META_VERSION, cp, rank, block_t, block_n, device, n_docs};
+  std::string key(sizeof(head) + size_t(n_docs) * sizeof(int32_t), '\0');
+  std::memcpy(&key[0], head, sizeof(head));
+  std::memcpy(&key[sizeof(head)], seqlens, size_t(n_docs) * sizeof(int32_t));
+  return key;
+}
+
+const MetaEntry& entry_of(const thd_meta* meta) {
+  if (meta == nullptr || !meta->entry || !meta->entry->plan) fail(THD_EINVAL, "meta is NULL");
+  return *meta->entry;
+}
+
+void check_ptr(const void* p, const char* name, size_t align) {
+  if (p == nullptr) fail(THD_EINVAL, std::string(name) + " is NULL");
+  if (reinterpret_cast<uintptr_t>(p) % align != 0)
+    fail(THD_EALIGN, std::string(name) + " is not " + std::to_string(align) + "-byte aligned");
+}
+
+const DeviceMeta& device_meta(const MetaEntry& e) {
+  if (e.dev.base == nullptr)
+    fail(THD_EMISMATCH, "metadata was built without a device copy (device = -1)");
+  int cur = -1;
+  check_hip(hipGetDevice(&cur), "hipGetDevice");
+  if (cur != e.dev.device)
+    fail(THD_EMISMATCH, "metadata lives on device " + std::to_string(e.dev.device) +
+                            " but the current device is " + std::to_string(cur));
+  return e.dev;
+}
+
+int preferred_block_t(int32_t group) { return kRowsPerWg / group; }
+
+void check_heads(int32_t hq, int32_t hkv) {
+  if (hq < 1 || hkv < 1) fail(THD_EINVAL, "head counts must be >= 1");
+  if (hq % hkv != 0) fail(THD_EINVAL, "hq must be a multiple of hkv");
+  if (hq / hkv > kRowsPerWg) fail(THD_EUNSUPPORTED, "hq / hkv must be <= 128");
+}
+
+void check_scale(float scale) {
+  if (!(std::isfinite(scale) && scale > 0.0f)) fail(THD_EINVAL, "softmax_scale must be finite and > 0");
+}
+
+void check_tiles(const Plan& p, int32_t group) {
+  if (p.block_n != kBlockN)
+    fail(THD_EMISMATCH, "metadata block_n " + std::to_string(p.block_n) + " != kernel's " +
+                            std::to_string(kBlockN));
+  if (int64_t(p.block_t) * group > kRowsPerWg)
+    fail(THD_EMISMATCH, "metadata block_t " + std::to_string(p.block_t) + " times group " +
+                            std::to_string(group) + " exceeds 128 rows");
+}
+
+}  // namespace
+
+MetaEntry::~MetaEntry() {
+  if (dev.base != nullptr) {
+    int saved = -1;
+    if (hipGetDevice(&saved) == hipSuccess) {
+      if (saved != dev.device) (void)hipSetDevice(dev.device);
+      (void)hipFree(dev.base);
+      if (saved != dev.device) (void)hipSetDevice(saved);
+    }
+  }
+}
+
+}  // namespace thd
+
+using namespace thd;
+
+extern "C" {
+
+const char* thd_last_error(void) { return g_last_error.c_str(); }
+
+int thd_plan_partition(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank,
+                       int64_t* total_tokens, int64_t* local_tokens, int32_t* q_global,
+                       int32_t* kv_row, int32_t* chunk_off) {
+  return guarded([&] {
+    const int64_t total = validate_partition(seqlens, n_docs, cp, rank);
+    if (total_tokens != nullptr) *total_tokens = total;
+    if (local_tokens != nullptr) *local_tokens = total / cp;
+    plan_partition(seqlens, n_docs, cp, rank, q_global, kv_row, chunk_off);
+  });
+}
+
+int thd_build_metadata(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank,
+                       int32_t block_t, int32_t block_n, int32_t device, thd_meta** out) {
+  return guarded([&] {
+    if (out == nullptr) fail(THD_EINVAL, "out is NULL");
+    *out = nullptr;
+    validate_partition(seqlens, n_docs, cp, rank);
+    if (device < -1) fail(THD_EINVAL, "device must be >= -1");
+    if (device >= 0) {
+      int count = 0;
+      check_hip(hipGetDeviceCount(&count), "hipGetDeviceCount");
+      if (device >= count) fail(THD_EINVAL, "no such device " + std::to_string(device));
+    }
+    const std::string key = make_key(seqlens, n_docs, cp, rank, block_t, block_n, device);
+    Cache& c = cache();
+    std::lock_guard<std::mutex> lock(c.mu);
+    auto hit = c.map.find(key);
+    auto handle = std::make_unique<thd_meta>();
+    if (hit != c.map.end()) {
+      ++c.hits;
+      c.lru.splice(c.lru.begin(), c.lru, c.where[key]);
+      handle->entry = hit->second;
+      handle->cache_hit = true;
+    } else {
+      ++c.misses;
+      auto e = std::make_shared<MetaEntry>();
+      e->plan = build_plan(seqlens, n_docs, cp, rank, block_t, block_n);
+      if (device >= 0) {
+        upload(*e, device);
+        ++c.uploads;
+      }
+      c.map.emplace(key, e);
+      c.lru.push_front(key);
+      c.where[key] = c.lru.begin();
+      while (c.map.size() > Cache::kCapacity) {
+        const std::string& victim = c.lru.back();
+        c.map.erase(victim);
+        c.where.erase(victim);
+        c.lru.pop_back();
+      }
+      handle->entry = std::move(e);
+    }
+    *out = handle.release();
+  });
+}
+
+int thd_meta_info(const thd_meta* meta, thd_meta_info_t* info) {
+  return guarded([&] {
+    const MetaEntry& e = entry_of(meta);
+    if (info == nullptr) fail(THD_EINVAL, "info is NULL");
+    const Plan& p = *e.plan;
+    info->total_tokens = p.total;
+    info->local_tokens = p.local;
+    info->n_tiles = int64_t(p.tiles.size() / 8);
+    info->n_kvtiles = int64_t(p.kvtiles.size() / 8);
+    info->useful_pairs = p.useful_pairs;
+    info->max_kv_tiles = p.max_kv_tiles;
+    info->n_docs = int32_t(p.seqlens.size());
+    info->cp = p.cp;
+    info->rank = p.rank;
+    info->block_t = p.block_t;
+    info->block_n = p.block_n;
+    info->version = THD_META_VERSION;
+    info->device = e.dev.base != nullptr ? e.dev.device : -1;
+    info->cache_hit = meta->cache_hit ? 1 : 0;
+  });
+}
+
+int thd_meta_copy(const thd_meta* meta, int32_t field, int32_t* dst, int64_t count) {
+  return guarded([&] {
+    const Plan& p = *entry_of(meta).plan;
+    const std::vector<int32_t>* src = nullptr;
+    switch (field) {
+      case THD_FIELD_Q_GLOBAL: src = &p.q_global; break;
+      case THD_FIELD_KV_ROW: src = &p.kv_row; break;
+      case THD_FIELD_CHUNK_OFF: src = &p.chunk_off; break;
+      case THD_FIELD_TILES: src = &p.tiles; break;
+      case THD_FIELD_ORDER: src = &p.order; break;
+      case THD_FIELD_KVTILES: src = &p.kvtiles; break;
+      default: fail(THD_EINVAL, "unknown field " + std::to_string(field));
+    }
+    if (count != int64_t(src->size()))
+      fail(THD_EINVAL, "count " + std::to_string(count) + " != field length " +
+                           std::to_string(src->size()));
+    if (count > 0 && dst == nullptr) fail(THD_EINVAL, "dst is NULL");
+    if (count > 0) std::memcpy(dst, src->data(), size_t(count) * sizeof(int32_t));
+  });
+}
+
+void thd_meta_release(thd_meta* meta) {
+  if (meta == nullptr) return;
+  std::lock_guard<std::mutex> lock(cache().mu);
+  delete meta;
+}
+
+int thd_cache_stats(int64_t* hits, int64_t* misses, int64_t* uploads, int64_t* entries) {
+  return guarded([&] {
+    Cache& c = cache();
+    std::lock_guard<std::mutex> lock(c.mu);
+    if (hits) *hits = c.hits;
+    if (misses) *misses = c.misses;
+    if (uploads) *uploads = c.uploads;
+    if (entries) *entries = int64_t(c.map.size());
+  });
+}
+
+int thd_cache_clear(void) {
+  return guarded([&] {
+    Cache& c = cache();
+    std::lock_guard<std::mutex> lock(c.mu);
+    c.map.clear();
+    c.where.clear();
+    c.lru.clear();
+    c.hits = c.misses = c.uploads = 0;
+  });
+}
+
+int thd_preferred_tiles(int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v, int32_t* block_t,
+                        int32_t* block_n) {
+  return guarded([&] {
+    check_heads(hq, hkv);
+    if (!fwd_supported(d_qk, d_v))
+      fail(THD_EUNSUPPORTED, "no kernel for d_qk=" + std::to_string(d_qk) +
+                                 ", d_v=" + std::to_string(d_v));
+    if (block_t == nullptr || block_n == nullptr) fail(THD_EINVAL, "output pointer is NULL");
+    *block_t = preferred_block_t(hq / hkv);
+    *block_n = kBlockN;
+  });
+}
+
+int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void* v, void* o,
+                 float* lse, int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
+                 float softmax_scale, void* hip_stream) {
+  return guarded([&] {
+    const MetaEntry& e = entry_of(meta);
+    const Plan& p = *e.plan;
+    check_heads(hq, hkv);
+    if (!fwd_supported(d_qk, d_v))
+      fail(THD_EUNSUPPORTED, "no forward kernel for d_qk=" + std::to_string(d_qk) +
+                                 ", d_v=" + std::to_string(d_v));
+    check_scale(softmax_scale);
+    const int32_t group = hq / hkv;
+    check_tiles(p, group);
+    check_ptr(q, "q", 16);
+    check_ptr(k, "k", 16);
+    check_ptr(v, "v", 16);
+    check_ptr(o, "o", 16);
+    check_ptr(lse, "lse", 16);
+    const DeviceMeta& d = device_meta(e);
+    const int64_t n_tiles = int64_t(p.tiles.size() / 8);
+    if (n_tiles * hkv >= (int64_t(1) << 31)) fail(THD_ERANGE, "grid too large");
+    FwdParams fp{};
+    fp.q = q;
+    fp.k = k;
+    fp.v = v;
+    fp.o = o;
+    fp.lse = lse;
+    fp.tiles = d.tiles;
+    fp.order = d.order;
+    fp.kv_row = d.kv_row;
+    fp.n_tiles = int32_t(n_tiles);
+    fp.hq = hq;
+    fp.hkv = hkv;
+    fp.group = group;
+    fp.block_t = p.block_t;
+    fp.total = p.total;
+    fp.scale_log2 = softmax_scale * 1.4426950408889634f;
+    check_hip(hipError_t(launch_fwd(fp, d_qk, d_v, hip_stream)), "forward launch");
+  });
+}
+
+int thd_attn_bwd_workspace(const thd_meta* meta, int32_t hq, int64_t* bytes) {
+  return guarded([&] {
+    const Plan& p = *entry_of(meta).plan;
+    if (hq < 1) fail(THD_EINVAL, "hq must be >= 1");
+    if (bytes == nullptr) fail(THD_EINVAL, "bytes is NULL");
+    *bytes = (p.local * hq * int64_t(sizeof(float)) + 255) / 256 * 256;
+  });
+}
+
+int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void* v, const void* o,
+                 const float* lse, const void* d_o, float* dq, float* dk, float* dv, int32_t hq,
+                 int32_t hkv, int32_t d_qk, int32_t d_v, float softmax_scale, void* workspace,
+                 int64_t workspace_bytes, void* hip_stream) {
+  return guarded([&] {
+    const MetaEntry& e = entry_of(meta);
+    const Plan& p = *e.plan;
+    check_heads(hq, hkv);
+    if (!bwd_supported(d_qk, d_v))
+      fail(THD_EUNSUPPORTED, "no backward kernel for d_qk=" + std::to_string(d_qk) +
+                                 ", d_v=" + std::to_string(d_v));
+    check_scale(softmax_scale);
+    const int32_t group = hq / hkv;
+    check_tiles(p, group);
+    check_ptr(q, "q", 16);
+    check_ptr(k, "k", 16);
+    check_ptr(v, "v", 16);
+    check_ptr(o, "o", 16);
+    check_ptr(lse, "lse", 16);
+    check_ptr(d_o, "d_o", 16);
+    check_ptr(dq, "dq", 16);
+    check_ptr(dk, "dk", 16);
+    check_ptr(dv, "dv", 16);
+    check_ptr(workspace, "workspace", 16);
+    const int64_t need = (p.local * hq * int64_t(sizeof(float)) + 255) / 256 * 256;
+    if (workspace_bytes < need)
+      fail(THD_EINVAL, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
+                           std::to_string(need));
+    const DeviceMeta& d = device_meta(e);
+    const int64_t n_tiles = int64_t(p.tiles.size() / 8);
+    const int64_t n_kvtiles = int64_t(p.kvtiles.size() / 8);
+    if (n_tiles * hkv >= (int64_t(1) << 31) || n_kvtiles * hkv >= (int64_t(1) << 31))
+      fail(THD_ERANGE, "grid too large");
+    BwdParams bp{};
+    bp.q = q;
+    bp.k = k;
+    bp.v = v;
+    bp.o = o;
+    bp.lse = lse;
+    bp.d_o = d_o;
+    bp.dq = dq;
+    bp.dk = dk;
+    bp.dv = dv;
+    bp.delta = static_cast<float*>(workspace);
+    bp.tiles = d.tiles;
+    bp.kvtiles = d.kvtiles;
+    bp.kv_row = d.kv_row;
+    bp.n_tiles = int32_t(n_tiles);
+    bp.n_kvtiles = int32_t(n_kvtiles);
+    bp.hq = hq;
+    bp.hkv = hkv;
+    bp.group = group;
+    bp.block_t = p.block_t;
+    bp.total = p.total;
+    bp.local = p.local;
+    bp.scale = softmax_scale;
+    bp.scale_log2 = softmax_scale * 1.4426950408889634f;
+    check_hip(hipError_t(launch_bwd(bp, d_qk, d_v, hip_stream)), "backward launch");
+  });
+}
+
+}  // extern "C"

@@ -1,0 +1,164 @@
+"""Forward parity of the HIP path against the fp64 oracle, on an MI355X.
+
+Small cases are compared element by element over every output; the full-size
+workloads are compared on sampled rows the oracle computes one at a time, and
+on properties that hold at any size (document-start rows, EOD isolation,
+causality, determinism, union over ranks).
+"""
+import numpy as np
+import pytest
+import torch
+
+import workloads
+from oracle import attention as oatt
+from oracle import partition as opart
+from parity import LSE_ABS, assert_close, device, sample_rows, to64
+
+pytestmark = pytest.mark.gpu
+
+thd = pytest.importorskip("packed_sequence_causal_amd")
+
+
+def _run(batch, rank=None, scale=None):
+    w = batch.workload
+    r = w.rank if rank is None else rank
+    dev = device()
+    q = batch.q.to(dev)
+    k = batch.k.to(dev)
+    v = batch.v.to(dev)
+    print(f"[fwd] case={w.name} lengths[:4]={batch.lengths[:4].tolist()} n={len(batch.lengths)} "
+          f"cp={w.cp} rank={r} hq={w.hq} hkv={w.hkv} dqk={w.d_qk} dv={w.d_v}", flush=True)
+    o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=batch.lengths, cp=w.cp, rank=r,
+                          softmax_scale=scale)
+    torch.cuda.synchronize()
+    return o, lse
+
+
+SMALL = [
+    # (seed, lengths, cp, rank, hq, hkv, dqk, dv)
+    (11, [256, 512, 256], 2, 0, 8, 8, 64, 64),
+    (12, [256, 512, 256], 2, 1, 8, 8, 64, 64),
+    (13, [8, 24, 40, 136, 520], 4, 1, 32, 8, 128, 128),
+    (14, [16, 32, 1040, 16, 400], 8, 3, 16, 16, 192, 128),
+    (15, [16 * x for x in (1, 2, 3, 5, 8, 13, 21, 32, 7, 4)], 8, 0, 64, 8, 128, 128),
+    (16, [1000, 72, 600], 4, 2, 32, 8, 128, 128),
+    (17, [36, 300, 84], 3, 2, 12, 4, 128, 128),        # group 3: 126 of 128 rows used
+    (18, [2, 4, 6, 2], 1, 0, 4, 2, 128, 128),          # cp = 1, documents shorter than a tile
+    (19, [4096], 2, 1, 4, 1, 64, 64),                  # one long document, group 4, MQA-like
+    (20, [32, 64], 2, 1, 32, 2, 128, 128),             # group 16: 8 tokens per tile
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: f"seed{c[0]}")
+def test_forward_matches_oracle_small(case):
+    seed, lengths, cp, rank, hq, hkv, dqk, dv = case
+    b = workloads.small_case(seed, lengths, cp, hq, hkv, dqk, dv, rank=rank)
+    o, lse = _run(b)
+    want_o, want_lse = oatt.attn_fwd64(to64(b.q), to64(b.k), to64(b.v), lengths, cp, rank)
+    assert_close(to64(o), want_o, "O")
+    assert_close(lse.cpu().double().numpy(), want_lse, "LSE", max_abs=LSE_ABS, mean_abs=LSE_ABS)
+
+
+def test_forward_custom_scale():
+    b = workloads.small_case(21, [64, 192], 2, 8, 2, 128, 128, rank=1)
+    o, lse = _run(b, scale=0.3)
+    want_o, want_lse = oatt.attn_fwd64(to64(b.q), to64(b.k), to64(b.v), b.lengths, 2, 1, scale=0.3)
+    assert_close(to64(o), want_o, "O")
+    assert_close(lse.cpu().double().numpy(), want_lse, "LSE", max_abs=LSE_ABS, mean_abs=LSE_ABS)
+
+
+@pytest.mark.parametrize("w", workloads.WORKLOADS, ids=lambda w: w.name)
+def test_forward_full_size_sampled_rows(w):
+    b = workloads.make_batch(w)
+    o, lse = _run(b)
+    qg = opart.q_global(b.lengths, w.cp, w.rank)
+    cu = opart.cu_seqlens(b.lengths)
+    rows = sample_rows(w.t_local, qg, cu, 48, w.index)
+    want_o, want_lse = oatt.attn_fwd64_rows(b.q.float().numpy(), b.k.float().numpy(),
+                                            b.v.float().numpy(), b.lengths, w.cp, w.rank, rows)
+    assert_close(to64(o[torch.from_numpy(rows).to(o.device)]), want_o, f"{w.name} O rows")
+    assert_close(lse[torch.from_numpy(rows).to(o.device)].cpu().double().numpy(), want_lse,
+                 f"{w.name} LSE rows", max_abs=LSE_ABS, mean_abs=LSE_ABS)
+    assert torch.isfinite(o.float()).all().item()
+    # rows that are a document's first token see one key: O equals V exactly
+    if w.rank == 0:
+        starts = [qg.tolist().index(c) for c in cu[:-1]]
+        rows_v = opart.kv_row(b.lengths, w.cp)[cu[:-1]]
+        group = w.hq // w.hkv
+        got = o[torch.tensor(starts, device=o.device)].cpu()
+        want = b.v[torch.from_numpy(rows_v.astype(np.int64))].repeat_interleave(group, dim=1)
+        assert torch.equal(got, want)
+
+
+def test_forward_tiny_full_compare():
+    w = workloads.BY_NAME["tiny"]
+    b = workloads.make_batch(w)
+    o, lse = _run(b)
+    want_o, want_lse = oatt.attn_fwd64(to64(b.q), to64(b.k), to64(b.v), b.lengths, w.cp, w.rank)
+    assert_close(to64(o), want_o, "O")
+    assert_close(lse.cpu().double().numpy(), want_lse, "LSE", max_abs=LSE_ABS, mean_abs=LSE_ABS)
+
+
+def test_forward_deterministic_and_isolated():
+    lengths, cp, rank = [64, 320, 128], 2, 0
+    b = workloads.small_case(30, lengths, cp, 32, 8, 128, 128, rank=rank)
+    o1, l1 = _run(b)
+    o2, l2 = _run(b)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    # EOD isolation: NaN in every other document's K/V leaves document 1's rows bit-identical
+    rows = opart.kv_row(lengths, cp)
+    cu = opart.cu_seqlens(lengths)
+    others = np.concatenate([rows[cu[0]:cu[1]], rows[cu[2]:cu[3]]]).astype(np.int64)
+    k2, v2 = b.k.clone(), b.v.clone()
+    k2[torch.from_numpy(others)] = float("nan")
+    v2[torch.from_numpy(others)] = float("nan")
+    b2 = workloads.Batch(b.workload, b.lengths, b.q, k2, v2)
+    o3, l3 = _run(b2)
+    qg = opart.q_global(lengths, cp, rank)
+    mine = torch.from_numpy(np.nonzero((qg >= cu[1]) & (qg < cu[2]))[0]).to(o1.device)
+    assert torch.equal(o3[mine], o1[mine]) and torch.equal(l3[mine], l1[mine])
+    # causality: changing keys after position 330 (inside a query tile of rank 0's
+    # chunk [304, 384)) leaves rows at or before 330 bit-identical
+    k4, v4 = b.k.clone(), b.v.clone()
+    later = torch.from_numpy(rows[331:cu[2]].astype(np.int64))
+    k4[later] = -k4[later] * 3
+    v4[later] = v4[later] + 1
+    o4, l4 = _run(workloads.Batch(b.workload, b.lengths, b.q, k4, v4))
+    early = torch.from_numpy(np.nonzero(qg <= 330)[0]).to(o1.device)
+    assert torch.equal(o4[early], o1[early]) and torch.equal(l4[early], l1[early])
+
+
+def test_union_over_ranks_is_unpartitioned_attention():
+    lengths, cp, hq, hkv = [64, 256, 128, 32], 4, 16, 4
+    total = sum(lengths)
+    rng = np.random.default_rng(31)
+    qglob = workloads.bf16_normal(rng, (total, hq, 128))
+    kglob = workloads.bf16_normal(rng, (total, hkv, 128))
+    vglob = workloads.bf16_normal(rng, (total, hkv, 128))
+    order = torch.from_numpy(opart.gathered_order(lengths, cp).astype(np.int64))
+    k = kglob[order].contiguous()
+    v = vglob[order].contiguous()
+    out = torch.zeros((total, hq, 128), dtype=torch.float64)
+    for r in range(cp):
+        qg = torch.from_numpy(opart.q_global(lengths, cp, r).astype(np.int64))
+        w = workloads.Workload("union", 31, total, cp, r, hq, hkv, 128, 128, "fixed",
+                               fixed=tuple(lengths))
+        o, _ = _run(workloads.Batch(w, np.asarray(lengths, np.int32), qglob[qg].contiguous(), k, v))
+        out[qg] = o.double().cpu()
+    # cp = 1 is the unpartitioned sequence: global order for Q, K and V
+    want, _ = oatt.attn_fwd64(to64(qglob), to64(kglob), to64(vglob), lengths, 1, 0)
+    assert_close(out.numpy(), want, "union O")
+
+
+def test_forward_reports_errors_from_device_path():
+    b = workloads.small_case(40, [64], 2, 8, 8, 128, 128, rank=0)
+    dev = device()
+    q, k, v = b.q.to(dev), b.k.to(dev), b.v.to(dev)
+    # metadata built for another group size is refused before launch
+    meta = thd.build_metadata(seqlens=b.lengths, cp=2, rank=0, block_t=128, block_n=64, device=0)
+    with pytest.raises(thd.ThdError) as err:
+        thd.attn_fwd(q=q[:, :8].contiguous(), k=k[:, :1].contiguous(), v=v[:, :1].contiguous(),
+                     seqlens=b.lengths, cp=2, rank=0, meta=meta)
+    assert err.value.status == "THD_EMISMATCH"
+    with pytest.raises(thd.ThdError):
+        thd.attn_fwd(q=q, k=k[:-2], v=v[:-2], seqlens=b.lengths, cp=2, rank=0)

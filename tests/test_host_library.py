@@ -1,0 +1,221 @@
+"""The C-ABI library on the CPU: exports, host planner, metadata cache.
+
+No device compute runs here; metadata is built host-only (device = -1).
+The planner must match the oracle bit for bit.
+"""
+import ctypes
+import os
+import re
+import threading
+
+import numpy as np
+import pytest
+
+import packed_sequence_causal_amd as thd
+import workloads
+from oracle import metadata as ometa
+from oracle import partition as opart
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    text = open(os.path.join(ROOT, "include", "thdattn.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(thd_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert len(declared) >= 12
+    lib = ctypes.CDLL(thd.LIB_PATH)
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert sorted(thd.EXPORTS) == declared
+
+
+def _compare_plan(lengths, cp, rank, bt, bn):
+    m = thd.build_metadata(seqlens=lengths, cp=cp, rank=rank, block_t=bt, block_n=bn)
+    assert np.array_equal(m.field("q_global"), opart.q_global(lengths, cp, rank))
+    assert np.array_equal(m.field("kv_row"), opart.kv_row(lengths, cp))
+    assert np.array_equal(m.field("chunk_off"), opart.chunk_off(lengths, cp))
+    tt = ometa.tiles(lengths, cp, rank, bt, bn)
+    assert np.array_equal(m.field("tiles"), tt)
+    assert np.array_equal(m.field("order"), ometa.order(tt))
+    assert np.array_equal(m.field("kvtiles"), ometa.kvtiles(lengths, cp, rank, bt, bn))
+    info = m.info()
+    assert info["useful_pairs"] == ometa.useful_pairs_closed_form(lengths, cp)
+    assert info["max_kv_tiles"] == int(tt[:, 6].max())
+    assert info["version"] == ometa.VERSION == thd.META_VERSION
+    plan = thd.plan_partition(seqlens=lengths, cp=cp, rank=rank)
+    assert np.array_equal(plan["q_global"], m.field("q_global"))
+    assert np.array_equal(plan["kv_row"], m.field("kv_row"))
+    assert np.array_equal(plan["chunk_off"], m.field("chunk_off"))
+
+
+@pytest.mark.parametrize("w", workloads.WORKLOADS, ids=lambda w: w.name)
+def test_metadata_bit_exact_on_workloads(w):
+    lengths = workloads.draw_lengths(w, np.random.default_rng(w.index))
+    bt, bn = thd.preferred_tiles(hq=w.hq, hkv=w.hkv, d_qk=w.d_qk, d_v=w.d_v)
+    ranks = sorted({w.rank, 0, w.cp - 1})
+    for rank in ranks:
+        _compare_plan(lengths, w.cp, rank, bt, bn)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_metadata_bit_exact_random(seed):
+    rng = np.random.default_rng(1000 + seed)
+    cp = int(rng.choice([1, 2, 3, 4, 8]))
+    lengths = workloads.random_lengths(rng, int(rng.integers(1, 9)), cp, 40)
+    bt = int(rng.choice([1, 3, 16, 32, 128]))
+    bn = int(rng.choice([1, 5, 64]))
+    _compare_plan(lengths, cp, int(rng.integers(0, cp)), bt, bn)
+
+
+def test_preferred_tiles():
+    assert thd.preferred_tiles(hq=32, hkv=8, d_qk=128, d_v=128) == (32, 64)
+    assert thd.preferred_tiles(hq=64, hkv=8, d_qk=128, d_v=128) == (16, 64)
+    assert thd.preferred_tiles(hq=16, hkv=16, d_qk=192, d_v=128) == (128, 64)
+    assert thd.preferred_tiles(hq=8, hkv=8, d_qk=64, d_v=64) == (128, 64)
+    assert thd.preferred_tiles(hq=12, hkv=4, d_qk=128, d_v=128) == (42, 64)
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    (dict(seqlens=[6, 8], cp=2, rank=0), "THD_ENOTDIV"),
+    (dict(seqlens=[8], cp=2, rank=2), "THD_ERANGE"),
+    (dict(seqlens=[8], cp=2, rank=-1), "THD_ERANGE"),
+    (dict(seqlens=[8], cp=0, rank=0), "THD_ERANGE"),
+    (dict(seqlens=[0, 8], cp=2, rank=0), "THD_EINVAL"),
+    (dict(seqlens=[-4], cp=2, rank=0), "THD_EINVAL"),
+    (dict(seqlens=[], cp=1, rank=0), "THD_EINVAL"),
+    (dict(seqlens=[2 ** 30, 2 ** 30], cp=1, rank=0), "THD_ERANGE"),
+])
+def test_partition_errors(kwargs, status):
+    with pytest.raises(thd.ThdError) as err:
+        thd.plan_partition(**kwargs)
+    assert err.value.status == status
+    assert str(err.value)
+    with pytest.raises(thd.ThdError) as err:
+        thd.build_metadata(block_t=4, block_n=4, **kwargs)
+    assert err.value.status == status
+
+
+def test_metadata_argument_errors():
+    for bt, bn in ((0, 4), (4, 0), (4, 5000)):
+        with pytest.raises(thd.ThdError) as err:
+            thd.build_metadata(seqlens=[8], cp=1, rank=0, block_t=bt, block_n=bn)
+        assert err.value.status == "THD_ERANGE"
+    with pytest.raises(thd.ThdError) as err:
+        thd.build_metadata(seqlens=[8], cp=1, rank=0, block_t=4, block_n=4, device=-2)
+    assert err.value.status == "THD_EINVAL"
+    for kw, status in ((dict(hq=12, hkv=5), "THD_EINVAL"), (dict(hq=0, hkv=1), "THD_EINVAL"),
+                       (dict(hq=256, hkv=1), "THD_EUNSUPPORTED")):
+        with pytest.raises(thd.ThdError) as err:
+            thd.preferred_tiles(d_qk=128, d_v=128, **kw)
+        assert err.value.status == status
+    with pytest.raises(thd.ThdError) as err:
+        thd.preferred_tiles(hq=8, hkv=8, d_qk=96, d_v=96)
+    assert err.value.status == "THD_EUNSUPPORTED"
+
+
+def test_null_pointers_return_errors():
+    lib = thd._lib
+    assert lib.thd_plan_partition(None, 1, 1, 0, None, None, None, None, None) == -1
+    assert lib.thd_build_metadata(None, 1, 1, 0, 1, 1, -1, None) == -1
+    assert lib.thd_meta_info(None, None) == -1
+    assert lib.thd_meta_copy(None, 0, None, 0) == -1
+    lib.thd_meta_release(None)
+    assert lib.thd_attn_fwd(None, None, None, None, None, None, 1, 1, 128, 128, 1.0, None) == -1
+    assert b"NULL" in lib.thd_last_error()
+    m = thd.build_metadata(seqlens=[8], cp=1, rank=0, block_t=4, block_n=64)
+    n = ctypes.c_int32()
+    # wrong count and unknown field
+    assert lib.thd_meta_copy(m.handle, 0, ctypes.byref(n), 1) == -1
+    assert lib.thd_meta_copy(m.handle, 9, ctypes.byref(n), 1) == -1
+
+
+def test_forward_rejects_host_only_metadata_and_bad_arguments():
+    m = thd.build_metadata(seqlens=[256], cp=1, rank=0, block_t=32, block_n=64)
+    buf = ctypes.create_string_buffer(1 << 16)
+    ptr = (ctypes.addressof(buf) + 15) // 16 * 16
+    lib = thd._lib
+    args = [m.handle, ptr, ptr, ptr, ptr, ptr]
+    # unsupported head dims are refused before any device check
+    assert lib.thd_attn_fwd(*args, 32, 8, 96, 96, 0.1, None) == -8
+    # bad scale
+    assert lib.thd_attn_fwd(*args, 32, 8, 128, 128, 0.0, None) == -1
+    assert lib.thd_attn_fwd(*args, 32, 8, 128, 128, float("nan"), None) == -1
+    # tile sizes that do not fit the group size
+    assert lib.thd_attn_fwd(*args, 64, 8, 128, 128, 0.1, None) == -5
+    # misaligned pointer
+    assert lib.thd_attn_fwd(m.handle, ptr + 2, ptr, ptr, ptr, ptr, 32, 8, 128, 128, 0.1, None) == -4
+    # host-only metadata cannot launch
+    assert lib.thd_attn_fwd(*args, 32, 8, 128, 128, 0.1, None) == -5
+    assert b"device" in lib.thd_last_error()
+
+
+def test_cache_hits_and_key_completeness():
+    thd.cache_clear()
+    a = thd.build_metadata(seqlens=[8, 16, 8], cp=2, rank=0, block_t=4, block_n=8)
+    b = thd.build_metadata(seqlens=[8, 16, 8], cp=2, rank=0, block_t=4, block_n=8)
+    assert a.info()["cache_hit"] == 0 and b.info()["cache_hit"] == 1
+    # same T and document count, different lengths: must miss and differ
+    c = thd.build_metadata(seqlens=[16, 8, 8], cp=2, rank=0, block_t=4, block_n=8)
+    assert c.info()["cache_hit"] == 0
+    assert not np.array_equal(a.field("q_global"), c.field("q_global"))
+    for kw in (dict(rank=1), dict(block_t=2), dict(block_n=4)):
+        args = dict(seqlens=[8, 16, 8], cp=2, rank=0, block_t=4, block_n=8)
+        args.update(kw)
+        assert thd.build_metadata(**args).info()["cache_hit"] == 0
+    st = thd.cache_stats()
+    assert st["hits"] == 1 and st["misses"] == 5 and st["uploads"] == 0
+    # a handle outlives the cache entry it came from
+    thd.cache_clear()
+    assert np.array_equal(a.field("tiles"), ometa.tiles([8, 16, 8], 2, 0, 4, 8))
+    a.release()
+    a.release()
+
+
+def test_cache_eviction_keeps_results_exact():
+    thd.cache_clear()
+    held = []
+    for i in range(80):
+        lengths = [8 * (1 + i % 7), 8 * (1 + i % 5)]
+        held.append((lengths, thd.build_metadata(seqlens=lengths, cp=2, rank=i % 2, block_t=4,
+                                                 block_n=8)))
+    assert thd.cache_stats()["entries"] <= 64
+    for i, (lengths, m) in enumerate(held):
+        assert np.array_equal(m.field("tiles"), ometa.tiles(lengths, 2, i % 2, 4, 8))
+
+
+def test_concurrent_builds_agree():
+    thd.cache_clear()
+    rng = np.random.default_rng(5)
+    cases = [workloads.random_lengths(rng, 6, 4, 30) for _ in range(4)]
+    errors = []
+    results = {}
+
+    def worker(tid):
+        try:
+            for rep in range(25):
+                idx = (tid + rep) % len(cases)
+                m = thd.build_metadata(seqlens=cases[idx], cp=4, rank=tid % 4, block_t=16,
+                                       block_n=64)
+                tiles = m.field("tiles")
+                results.setdefault((idx, tid % 4), tiles)
+                if not np.array_equal(results[(idx, tid % 4)], tiles):
+                    errors.append("mismatch")
+                m.release()
+        except Exception as exc:  # pragma: no cover - reported below
+            errors.append(repr(exc))
+
+    threads = [threading.Thread(target=worker, args=(t,)) for t in range(16)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not errors
+    st = thd.cache_stats()
+    assert st["misses"] == len({(i, r) for i in range(4) for r in range(4)} & set(results))
+    for (idx, rank), tiles in results.items():
+        assert np.array_equal(tiles, ometa.tiles(cases[idx], 4, rank, 16, 64))
