@@ -17,11 +17,13 @@
 //
 // Per KV tile of 64 keys (only the tiles from the document start up to the
 // tile's last row are visited):
-//   * the next tile's K rows and V rows are fetched with 16-byte global loads
-//     into registers while the current tile is computed; the row of each key
-//     comes from the gathered-row map (no reorder copy of K/V);
-//   * K is stored to LDS row-major, V transposed (V^T), so both MFMA operands
-//     read contiguous runs along the contraction dimension;
+//   * K and V rows are gathered straight from HBM into a two-stage LDS ring
+//     with global_load_lds_dwordx4 (16 bytes per lane, no register staging):
+//     the next tile streams in while the current one is computed. The row of
+//     each key comes from the gathered-row map (no reorder copy of K/V); those
+//     indices are fetched one tile further ahead. Rows are stored with their
+//     16-byte chunks XOR-swizzled by row so that the MFMA operand reads below
+//     hit distinct LDS banks;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (A = K from LDS, B = Q^T from
 //     registers): each lane then holds one query row (lane % 32) and 16 keys
 //     per 32-key block, so row reductions are in-lane plus one exchange with
@@ -32,7 +34,10 @@
 //     grows by more than 8 (2^8 headroom in fp32 and bf16), which skips most
 //     rescales of the accumulator and is exact up to rounding;
 //   * O^T += V^T P^T: the S^T register layout is already the B-operand layout
-//     of P^T, so P never leaves registers.
+//     of P^T, so P never leaves registers; the V^T operand is read from the
+//     row-major V tile with ds_read_b64_tr_b16, which hands each lane of a
+//     16-lane group one column of the 4 x 16 block formed by the group's four
+//     8-byte row pieces (4 consecutive keys of one V column).
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -45,45 +50,59 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __attribute__((address_space(3))) void lds_void;
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 constexpr int kThreads = kWaves * 64;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
+constexpr int kWaitVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0)
+
+// Position of 16-byte chunk c of LDS row r: c ^ swz(r). The XOR stays inside
+// an aligned group of 8 (or 16) chunks, so it never leaves the row.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (CPR == 16) {
+    return ((r & 3) << 2) | ((r >> 2) & 3);
+  } else {
+    return (r >> 1) & 7;
+  }
+}
 
 template <int DQK, int DV>
 struct FwdShape {
   static constexpr int BN = kBlockN;
-  static constexpr int KLD = DQK + 8;        // LDS K row stride (bf16), 16-byte pad
-  static constexpr int VLD = BN + 4;         // LDS V^T row stride (bf16), 8-byte pad
-  static constexpr int KCH = DQK / 8;        // 16-byte chunks per K row
-  static constexpr int K_LOADS = BN * KCH / kThreads;
-  static constexpr int V_CH = DV / 8;        // 16-byte chunks per V row
-  static constexpr int V_BLOCKS = (BN / 4) * V_CH;   // 4 keys x 8 dims each
-  static constexpr int V_LOADS = (V_BLOCKS + kThreads - 1) / kThreads;
+  static constexpr int KCPR = DQK / 8;            // 16-byte chunks per K row
+  static constexpr int VCPR = DV / 8;
+  static constexpr int KROWB = DQK * 2;
+  static constexpr int VROWB = DV * 2;
+  static constexpr int KBYTES = BN * KROWB;       // one K tile in LDS
+  static constexpr int VBYTES = BN * VROWB;
+  static constexpr int STAGE = KBYTES + VBYTES;
+  static constexpr int K_IPW = BN * KCPR / 64 / kWaves;   // 1 KB loads per wave per tile
+  static constexpr int V_IPW = BN * VCPR / 64 / kWaves;
+  static constexpr bool SAME_ROWS = (KCPR == VCPR);
+  static constexpr int NROWS = SAME_ROWS ? K_IPW : K_IPW + V_IPW;  // row indices per lane per tile
   static constexpr int KSTEPS = DQK / 16;
   static constexpr int DVB = DV / 32;
-  static_assert(BN * KCH % kThreads == 0, "K tile must split evenly over the workgroup");
+  static_assert(BN * KCPR % (64 * kWaves) == 0 && BN * VCPR % (64 * kWaves) == 0,
+                "tiles must split into whole 1 KB loads per wave");
   static_assert(DQK % 16 == 0 && DV % 32 == 0, "head dims must suit the MFMA tiles");
+  static_assert(KCPR == 8 || KCPR == 16 || KCPR == 24, "chunk swizzle needs 8, 16 or 24 chunks");
+  static_assert(VCPR == 8 || VCPR == 16, "V chunk swizzle needs 8 or 16 chunks");
 };
-
-__device__ __forceinline__ uint32_t lo_pair(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);   // a.lo16 | b.lo16 << 16
-}
-__device__ __forceinline__ uint32_t hi_pair(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);   // a.hi16 | b.hi16 << 16
-}
 
 template <int DQK, int DV>
 __global__ __launch_bounds__(kThreads, 2) void thd_fwd_kernel(FwdParams p) {
   using S = FwdShape<DQK, DV>;
   constexpr int BN = S::BN;
-  __shared__ __attribute__((aligned(16))) __bf16 ks[BN * S::KLD];
-  __shared__ __attribute__((aligned(16))) __bf16 vt[DV * S::VLD];
+  __shared__ __attribute__((aligned(1024))) char smem[2 * S::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int half = lane >> 5;        // which 32-lane half
   const int lrow = lane & 31;
 
@@ -96,7 +115,7 @@ __global__ __launch_bounds__(kThreads, 2) void thd_fwd_kernel(FwdParams p) {
   const int kv_start = td[5];
   const int n_kv = td[6];
   const int n_full = td[7];
-  const int key_end = q_glob0 + n_rows;    // keys from here on are seen by no row
+  const int key_last = q_glob0 + n_rows - 1;   // keys past this are seen by no row
 
   const int G = p.group;
   const int row = wave * 32 + lrow;
@@ -107,8 +126,9 @@ __global__ __launch_bounds__(kThreads, 2) void thd_fwd_kernel(FwdParams p) {
   const bool wave_active = (wave * 32) / G < n_rows;
 
   const __bf16* __restrict__ qp = static_cast<const __bf16*>(p.q);
-  const __bf16* __restrict__ kp = static_cast<const __bf16*>(p.k);
-  const __bf16* __restrict__ vp = static_cast<const __bf16*>(p.v);
+  const char* __restrict__ kb = static_cast<const char*>(p.k);
+  const char* __restrict__ vb = static_cast<const char*>(p.v);
+  const int32_t* __restrict__ kv_row = p.kv_row;
   const int hkv = p.hkv;
 
   // Q^T operand: lane holds Q[row][16*st + 8*half .. +7] for each k-step.
@@ -116,81 +136,55 @@ __global__ __launch_bounds__(kThreads, 2) void thd_fwd_kernel(FwdParams p) {
   {
     const __bf16* qrow = qp + (size_t(q_local0 + tok) * p.hq + head) * DQK + 8 * half;
 #pragma unroll
-    for (int st = 0; st < S::KSTEPS; ++st) {
-      if (valid) {
-        qf[st] = *reinterpret_cast<const bf16x8*>(qrow + 16 * st);
-      } else {
-        qf[st] = bf16x8{};
-      }
-    }
+    for (int st = 0; st < S::KSTEPS; ++st)
+      qf[st] = valid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * st) : bf16x8{};
   }
 
-  uint4 kreg[S::K_LOADS];
-  uint4 vreg[S::V_LOADS][4];
-
-  auto fetch = [&](int j) {
+  // Loader geometry: load i of this wave fills LDS bytes [1 KB * gi, +1 KB) of
+  // the K (or V) tile, gi = wave * IPW + i; lane l writes slot q = 64 gi + l,
+  // i.e. row q / CPR, chunk position q % CPR, holding global chunk
+  // (q % CPR) ^ swz(row).
+  int rows_cur[S::NROWS];   // gathered rows of this lane's keys, next tile to load
+  int rows_nxt[S::NROWS];   // ... and the tile after it
+  auto key_row = [&](int i) -> int {   // tile-relative row of this lane's load i
+    if (i < S::K_IPW) return ((wave * S::K_IPW + i) * 64 + lane) / S::KCPR;
+    return ((wave * S::V_IPW + (i - S::K_IPW)) * 64 + lane) / S::VCPR;
+  };
+  auto fetch_rows = [&](int j, int* rows) {
     const int key0 = kv_start + j * BN;
 #pragma unroll
-    for (int i = 0; i < S::K_LOADS; ++i) {
-      const int c = tid + kThreads * i;
-      const int r = c / S::KCH;
-      const int col = c - r * S::KCH;
-      const int key = key0 + r;
-      if (key < key_end) {
-        const int grow = p.kv_row[key];
-        kreg[i] = *reinterpret_cast<const uint4*>(kp + (size_t(grow) * hkv + kvh) * DQK + col * 8);
-      } else {
-        kreg[i] = uint4{0u, 0u, 0u, 0u};
-      }
+    for (int i = 0; i < S::NROWS; ++i) rows[i] = kv_row[min(key0 + key_row(i), key_last)];
+  };
+  auto issue_tile = [&](int j, const int* rows) {
+    char* stage = smem + (j & 1) * S::STAGE;
+#pragma unroll
+    for (int i = 0; i < S::K_IPW; ++i) {
+      const int q = (wave * S::K_IPW + i) * 64 + lane;
+      const int r = q / S::KCPR;
+      const int c = (q - r * S::KCPR) ^ swz<S::KCPR>(r);
+      const char* src = kb + (size_t(rows[i]) * hkv + kvh) * S::KROWB + c * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + (wave * S::K_IPW + i) * 1024), 16, 0, 0);
     }
 #pragma unroll
-    for (int i = 0; i < S::V_LOADS; ++i) {
-      const int blk = tid + kThreads * i;
-      const int dch = blk % S::V_CH;
-      const int quad = blk / S::V_CH;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int key = key0 + 4 * quad + e;
-        if (blk < S::V_BLOCKS && key < key_end) {
-          const int grow = p.kv_row[key];
-          vreg[i][e] = *reinterpret_cast<const uint4*>(vp + (size_t(grow) * hkv + kvh) * DV + dch * 8);
-        } else {
-          vreg[i][e] = uint4{0u, 0u, 0u, 0u};
-        }
-      }
+    for (int i = 0; i < S::V_IPW; ++i) {
+      const int q = (wave * S::V_IPW + i) * 64 + lane;
+      const int r = q / S::VCPR;
+      const int c = (q - r * S::VCPR) ^ swz<S::VCPR>(r);
+      const int grow = S::SAME_ROWS ? rows[i] : rows[S::K_IPW + i];
+      const char* src = vb + (size_t(grow) * hkv + kvh) * S::VROWB + c * 16;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + S::KBYTES + (wave * S::V_IPW + i) * 1024), 16, 0, 0);
     }
   };
 
-  auto stash = [&]() {
-#pragma unroll
-    for (int i = 0; i < S::K_LOADS; ++i) {
-      const int c = tid + kThreads * i;
-      const int r = c / S::KCH;
-      const int col = c - r * S::KCH;
-      *reinterpret_cast<uint4*>(&ks[r * S::KLD + col * 8]) = kreg[i];
-    }
-#pragma unroll
-    for (int i = 0; i < S::V_LOADS; ++i) {
-      const int blk = tid + kThreads * i;
-      if (blk < S::V_BLOCKS) {
-        const int dch = blk % S::V_CH;
-        const int quad = blk / S::V_CH;
-        const uint32_t w[4][4] = {{vreg[i][0].x, vreg[i][0].y, vreg[i][0].z, vreg[i][0].w},
-                                  {vreg[i][1].x, vreg[i][1].y, vreg[i][1].z, vreg[i][1].w},
-                                  {vreg[i][2].x, vreg[i][2].y, vreg[i][2].z, vreg[i][2].w},
-                                  {vreg[i][3].x, vreg[i][3].y, vreg[i][3].z, vreg[i][3].w}};
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-          // dims 2m and 2m+1 of the four keys, as 4 consecutive bf16 each
-          const uint2 even{lo_pair(w[0][m], w[1][m]), lo_pair(w[2][m], w[3][m])};
-          const uint2 odd{hi_pair(w[0][m], w[1][m]), hi_pair(w[2][m], w[3][m])};
-          const int d = dch * 8 + 2 * m;
-          *reinterpret_cast<uint2*>(&vt[d * S::VLD + 4 * quad]) = even;
-          *reinterpret_cast<uint2*>(&vt[(d + 1) * S::VLD + 4 * quad]) = odd;
-        }
-      }
-    }
-  };
+  // Per-lane LDS read offsets (relative to a stage).
+  // K operand: row 32*kb + lrow, chunk 2*st + half.
+  const int k_swz = swz<S::KCPR>(lrow);          // same for rows lrow and 32 + lrow
+  const int k_off = lrow * S::KROWB;
+  // V^T operand via transpose reads: lane (group g = lane/16, a = (lane%16)/4,
+  // c = lane%4) reads row 16t + 4*half + a (+8), columns 32b + 16(g%2) + 4c .. +3.
+  const int tr_a = (lane & 15) >> 2;
+  const int tr_c = lane & 3;
+  const int tr_dv = 16 * ((lane >> 4) & 1) + 4 * tr_c;     // plus 32*b
 
   f32x16 acc[S::DVB];
 #pragma unroll
@@ -199,79 +193,99 @@ __global__ __launch_bounds__(kThreads, 2) void thd_fwd_kernel(FwdParams p) {
   float l_run = 0.0f;        // this lane's share of the row's sum of 2^(...)
   const float c2 = p.scale_log2;
 
-  fetch(0);
+  // Prologue: rows of tiles 0 and 1, then tile 0's data.
+  fetch_rows(0, rows_cur);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  issue_tile(0, rows_cur);
+  if (n_kv > 1) fetch_rows(1, rows_cur);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+
   for (int j = 0; j < n_kv; ++j) {
-    if (j > 0) __syncthreads();
-    stash();
-    __syncthreads();
-    if (j + 1 < n_kv) fetch(j + 1);
-    if (!wave_active) continue;
+    // Stage j&1 holds tile j; rows_cur holds tile j+1's rows.
+    if (j + 1 < n_kv) issue_tile(j + 1, rows_cur);
+    if (j + 2 < n_kv) fetch_rows(j + 2, rows_nxt);
+    const char* stage = smem + (j & 1) * S::STAGE;
 
-    // S^T = K Q^T for keys [32*kb, 32*kb + 32) of the tile.
-    f32x16 s[2] = {f32x16{}, f32x16{}};
+    if (wave_active) {
+      // S^T = K Q^T for keys [32*kb, 32*kb + 32) of the tile.
+      f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
-    for (int st = 0; st < S::KSTEPS; ++st) {
+      for (int st = 0; st < S::KSTEPS; ++st) {
+        const int cpos = ((2 * st + half) ^ k_swz) * 16;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&ks[(32 * kb + lrow) * S::KLD + 16 * st + 8 * half]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb], 0, 0, 0);
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + k_off + 32 * kb2 * S::KROWB + cpos);
+          s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb2], 0, 0, 0);
+        }
       }
-    }
 
-    if (j >= n_full) {
-      const int key0 = kv_start + j * BN + 4 * half;
+      if (j >= n_full) {
+        const int key0 = kv_start + j * BN + 4 * half;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int key = key0 + 32 * kb2 + 8 * (r >> 2) + (r & 3);
+            if (key > qpos) s[kb2][r] = -INFINITY;
+          }
+      }
+
+      float mx = s[0][0];
+#pragma unroll
+      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      // Each row decides on its own (so a row's arithmetic never depends on
+      // its neighbours); the wave only skips the rescale when no row needs it.
+      const float m_tile = mx * c2;
+      const bool need = m_tile > m_run + kRescaleSlack;
+      if (__any(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.0f;
+#pragma unroll
+        for (int b = 0; b < S::DVB; ++b)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
+        l_run *= alpha;
+        m_run = need ? m_tile : m_run;
+      }
+
+      const float neg_m = -m_run;
+      bf16x8 pb[4];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * kb + 8 * (r >> 2) + (r & 3);
-          if (key > qpos) s[kb][r] = -INFINITY;
+          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r], c2, neg_m));
+          l_run += e;
+          pb[2 * kb2 + (r >> 3)][r & 7] = static_cast<__bf16>(e);
         }
-    }
 
-    float mx = s[0][0];
+      // O^T += V^T P^T, 16 keys per MFMA: keys 16t + 4*half + {0..3, 8..11}.
 #pragma unroll
-    for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
+      for (int t = 0; t < 4; ++t) {
+        const int r0 = 16 * t + 4 * half + tr_a;
+        const int r1 = r0 + 8;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // Each row decides on its own (so a row's arithmetic never depends on
-    // its neighbours); the wave only skips the rescale when no row needs it.
-    const float m_tile = mx * c2;
-    const bool need = m_tile > m_run + kRescaleSlack;
-    if (__any(need)) {
-      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.0f;
-#pragma unroll
-      for (int b = 0; b < S::DVB; ++b)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
-      l_run *= alpha;
-      m_run = need ? m_tile : m_run;
-    }
-
-    const float neg_m = -m_run;
-    bf16x8 pb[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][r], c2, neg_m));
-        l_run += e;
-        pb[2 * kb + (r >> 3)][r & 7] = static_cast<__bf16>(e);
-      }
-
-    // O^T += V^T P^T, 16 keys per MFMA: keys 16t + 4*half + {0..3, 8..11}.
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-#pragma unroll
-      for (int b = 0; b < S::DVB; ++b) {
-        const __bf16* src = &vt[(32 * b + lrow) * S::VLD + 16 * t + 4 * half];
-        const bf16x4 lo = *reinterpret_cast<const bf16x4*>(src);
-        const bf16x4 hi = *reinterpret_cast<const bf16x4*>(src + 8);
-        const bf16x8 a = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-        acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t], acc[b], 0, 0, 0);
+        for (int b = 0; b < S::DVB; ++b) {
+          const int dv = 32 * b + tr_dv;
+          const int off0 = S::KBYTES + r0 * S::VROWB + (((dv >> 3) ^ swz<S::VCPR>(r0)) << 4) + ((tr_c & 1) << 3);
+          const int off1 = S::KBYTES + r1 * S::VROWB + (((dv >> 3) ^ swz<S::VCPR>(r1)) << 4) + ((tr_c & 1) << 3);
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + off0));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + off1));
+          const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t], acc[b], 0, 0, 0);
+        }
       }
     }
+
+    // Tile j+1 (and tile j+2's rows) must have landed, and every wave must be
+    // done with stage j&1 before it is refilled.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < S::NROWS; ++i) rows_cur[i] = rows_nxt[i];
   }
 
   if (!wave_active) return;
