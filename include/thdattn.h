@@ -75,8 +75,10 @@ typedef enum {
  *                             up to the last row's position; the first
  *                             n_full_kv_tiles need no causal mask)
  *   ORDER     [n_tiles]       tile indices, most KV tiles first (ties by index)
- *   KVTILES   [n_kvtiles*8]   per key tile (backward): doc, kv_global_start,
- *                             n_keys, q_tile_begin, q_tile_end, 0, 0, 0 */
+ *   KVTILES   [n_kvtiles*8]   per key tile (backward; together they cover
+ *                             every key once): doc, kv_global_start, n_keys,
+ *                             q_tile_begin, q_tile_end (the query tiles that
+ *                             see the tile, empty for unseen keys), 0, 0, 0 */
 enum {
   THD_FIELD_Q_GLOBAL = 0,
   THD_FIELD_KV_ROW = 1,

@@ -24,14 +24,16 @@ order[n_tiles]: tile indices sorted by n_kv descending, ties by index
 ascending (largest work first). Parity unpinned: it is a scheduling choice with
 no truth outside this definition.
 
-kvtiles[m][8] (backward): for document i, j = 0 .. ceil((2cp-r)*c_i / BN) - 1:
+kvtiles[m][8] (backward): for document i, j = 0 .. ceil(L_i / BN) - 1:
     ks      = cu_i + j*BN
-    n_keys  = min(BN, (2cp-r)*c_i - j*BN)
+    n_keys  = min(BN, L_i - j*BN)
     q_begin = first tile of document i (natural index) whose last row's global
-              position is >= ks
+              position is >= ks, or q_end if there is none
     q_end   = one past the last tile of document i
     record  = [i, ks, n_keys, q_begin, q_end, 0, 0, 0]
-Keys of document i at offset >= (2cp-r)*c_i are seen by no local query.
+The key tiles cover every key once. Keys of document i at offset >=
+(2cp-r)*c_i are seen by no local query (the rank's later chunk is 2cp-1-r), so
+tiles made only of such keys get the empty range q_begin = q_end.
 """
 from __future__ import annotations
 
@@ -81,13 +83,11 @@ def kvtiles(seqlens, cp: int, rank: int, block_t: int, block_n: int) -> np.ndarr
     tt = tiles(lengths, cp, rank, block_t, block_n)
     rows = []
     for i, length in enumerate(lengths):
-        c = length // (2 * cp)
-        seen = (2 * cp - rank) * c
         doc_tiles = [t for t in range(tt.shape[0]) if int(tt[t, 3]) == i]
         q_end = doc_tiles[-1] + 1
-        for j in range(_ceil_div(seen, block_n)):
+        for j in range(_ceil_div(length, block_n)):
             ks = cu[i] + j * block_n
-            n_keys = min(block_n, seen - j * block_n)
+            n_keys = min(block_n, length - j * block_n)
             q_begin = q_end
             for t in doc_tiles:
                 if int(tt[t, 1]) + int(tt[t, 2]) - 1 >= ks:

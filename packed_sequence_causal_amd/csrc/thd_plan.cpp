@@ -123,18 +123,18 @@ std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t
     return p.tiles[size_t(a) * 8 + 6] > p.tiles[size_t(b) * 8 + 6];
   });
 
-  // Backward key tiles: keys of document i past offset (2cp-r)*c_i are seen by
-  // no local query (the rank's later chunk is 2cp-1-r). The query tiles seeing
-  // a key tile form a suffix of the document's tiles, found by one forward
-  // walk because tile end positions increase within a document.
+  // Backward key tiles cover every key of every document. The query tiles
+  // seeing a key tile form a suffix of the document's tiles, found by one
+  // forward walk because tile end positions increase within a document; keys
+  // past offset (2cp-r)*c_i are seen by no local query (the rank's later chunk
+  // is 2cp-1-r), so their tiles get an empty range.
   cu = 0;
   for (int32_t i = 0; i < n_docs; ++i) {
-    const int64_t c = seqlens[i] / (2 * cp);
-    const int64_t seen = (2 * cp - rank) * c;
+    const int64_t len = seqlens[i];
     int64_t qb = doc_first_tile[i];
-    for (int64_t j = 0; j * block_n < seen; ++j) {
+    for (int64_t j = 0; j * block_n < len; ++j) {
       const int64_t ks = cu + j * block_n;
-      const int64_t nk = std::min<int64_t>(block_n, seen - j * block_n);
+      const int64_t nk = std::min<int64_t>(block_n, len - j * block_n);
       while (qb < doc_end_tile[i] &&
              int64_t(p.tiles[size_t(qb) * 8 + 1]) + p.tiles[size_t(qb) * 8 + 2] - 1 < ks)
         ++qb;

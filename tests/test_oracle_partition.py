@@ -129,16 +129,22 @@ def test_tiles_cover_visible_pairs_exactly(lengths, cp, bt, bn):
         assert set(seen_b) == want
 
 
-def test_kvtiles_skip_only_unseen_keys():
+def test_kvtiles_cover_every_key_once():
     lengths, cp = [16, 32, 8], 2
+    cu = partition.cu_seqlens(lengths)
     for rank in range(cp):
         tt = metadata.tiles(lengths, cp, rank, 2, 4)
         kt = metadata.kvtiles(lengths, cp, rank, 2, 4)
         keys_seen = {key for _, key in _visible_pairs(lengths, cp, rank)}
-        covered = {key for doc, ks, nk, *_ in kt.tolist() for key in range(ks, ks + nk)}
-        assert covered == keys_seen
-        # the first q tile listed for a kv tile sees its first key, the one before it does not
+        covered = [key for doc, ks, nk, *_ in kt.tolist() for key in range(ks, ks + nk)]
+        assert covered == list(range(cu[-1]))
         for doc, ks, nk, qb, qe, *_ in kt.tolist():
+            assert cu[doc] <= ks and ks + nk <= cu[doc + 1]
+            if qb == qe:
+                # an empty range only for keys no local query sees
+                assert not keys_seen & set(range(ks, ks + nk))
+                continue
+            # the first q tile listed sees the tile's first key, the one before it does not
             assert tt[qb, 1] + tt[qb, 2] - 1 >= ks
             if qb > 0 and tt[qb - 1, 3] == doc:
                 assert tt[qb - 1, 1] + tt[qb - 1, 2] - 1 < ks
