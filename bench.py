@@ -139,7 +139,7 @@ def main(argv=None) -> int:
         thd.attn_fwd(q=q, k=k, v=v, seqlens=batch.lengths, cp=w.cp, rank=w.rank, out=o, lse=lse,
                      meta=meta)
         if w.backward:
-            thd.attn_bwd(q=q, k=k, v=v, o=o, lse=lse, d_o=do, seqlens=batch.lengths, cp=w.cp,
+            thd.attn_bwd(q=q, k=k, v=v, lse=lse, d_o=do, seqlens=batch.lengths, cp=w.cp,
                          rank=w.rank, meta=meta)
 
     # Parity gate: no throughput is reported for a path that disagrees with the oracle.

@@ -156,10 +156,13 @@ int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void*
 int thd_attn_bwd_workspace(const thd_meta* meta, int32_t hq, int64_t* bytes);
 
 /* Backward: dq, and this rank's partial dk, dv (all fp32, layouts above),
- * from the forward's o and lse and the upstream gradient d_o. dk and dv are
- * written in full (zeros for keys no local query sees). */
+ * from the forward's lse and the upstream gradient d_o. dk and dv are written
+ * in full (zeros for keys no local query sees). The softmax-gradient term
+ * D = rowsum(dO * O) is recomputed as rowsum(P * dP) from the scores, which is
+ * equal for the exact O, so the forward's rounded o is not an input. The
+ * workspace (size from thd_attn_bwd_workspace) holds D. */
 int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void* v,
-                 const void* o, const float* lse, const void* d_o,
+                 const float* lse, const void* d_o,
                  float* dq, float* dk, float* dv,
                  int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v, float softmax_scale,
                  void* workspace, int64_t workspace_bytes, void* hip_stream);

@@ -71,7 +71,7 @@ def _load():
         "thd_preferred_tiles": (ctypes.c_int, [i32, i32, i32, i32, pi32, pi32]),
         "thd_attn_fwd": (ctypes.c_int, [p, p, p, p, p, p, i32, i32, i32, i32, ctypes.c_float, p]),
         "thd_attn_bwd_workspace": (ctypes.c_int, [p, i32, pi64]),
-        "thd_attn_bwd": (ctypes.c_int, [p, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
+        "thd_attn_bwd": (ctypes.c_int, [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
                                         ctypes.c_float, p, i64, p]),
     }
     for name, (res, args) in sigs.items():
@@ -233,10 +233,11 @@ def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=No
     return out, lse
 
 
-def attn_bwd(*, q, k, v, o, lse, d_o, seqlens, cp: int, rank: int, softmax_scale=None,
+def attn_bwd(*, q, k, v, lse, d_o, seqlens, cp: int, rank: int, softmax_scale=None,
              stream=None, meta: Meta | None = None, workspace=None):
     """Backward for one rank. Returns (dq fp32, dk fp32, dv fp32); dk/dv are
-    this rank's partial sums in the gathered layout (zeros for unseen keys)."""
+    this rank's partial sums in the gathered layout (zeros for unseen keys).
+    lse is the forward's; the forward's O is not needed."""
     torch = _torch()
     hq, hkv, d_qk, d_v = q.shape[1], k.shape[1], q.shape[2], v.shape[2]
     device = q.device.index
@@ -254,7 +255,14 @@ def attn_bwd(*, q, k, v, o, lse, d_o, seqlens, cp: int, rank: int, softmax_scale
     dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
     dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
     scale = 1.0 / math.sqrt(d_qk) if softmax_scale is None else float(softmax_scale)
-    _check(_lib.thd_attn_bwd(meta.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+    for name, t in (("q", q), ("k", k), ("v", v), ("d_o", d_o)):
+        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 3:
+            raise ThdError(-1, f"{name} must be a contiguous 3-d bf16 device tensor")
+    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (q.shape[0], hq):
+        raise ThdError(-1, "lse must be a contiguous fp32 [T_local, Hq] tensor")
+    if tuple(d_o.shape) != (q.shape[0], hq, d_v):
+        raise ThdError(-5, "d_o must be [T_local, Hq, d_v]")
+    _check(_lib.thd_attn_bwd(meta.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                              lse.data_ptr(), d_o.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                              dv.data_ptr(), hq, hkv, d_qk, d_v, scale, workspace.data_ptr(),
                              workspace.numel(), _stream_handle(stream, q.device)))

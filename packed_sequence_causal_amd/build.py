@@ -44,6 +44,9 @@ def build(verbose: bool = False) -> str:
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{res.stdout}\n{res.stderr}")
+    # Loading resolves every symbol now: a missing kernel launch stub fails the build here.
+    import ctypes
+    ctypes.CDLL(os.path.abspath(tmp))
     os.replace(tmp, LIB)
     if verbose:
         print("built", LIB)

@@ -93,7 +93,6 @@ struct BwdParams {
   const void* q;
   const void* k;
   const void* v;
-  const void* o;
   const float* lse;
   const void* d_o;
   float* dq;

@@ -370,7 +370,7 @@ int thd_attn_bwd_workspace(const thd_meta* meta, int32_t hq, int64_t* bytes) {
   });
 }
 
-int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void* v, const void* o,
+int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void* v,
                  const float* lse, const void* d_o, float* dq, float* dk, float* dv, int32_t hq,
                  int32_t hkv, int32_t d_qk, int32_t d_v, float softmax_scale, void* workspace,
                  int64_t workspace_bytes, void* hip_stream) {
@@ -387,7 +387,6 @@ int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void*
     check_ptr(q, "q", 16);
     check_ptr(k, "k", 16);
     check_ptr(v, "v", 16);
-    check_ptr(o, "o", 16);
     check_ptr(lse, "lse", 16);
     check_ptr(d_o, "d_o", 16);
     check_ptr(dq, "dq", 16);
@@ -407,7 +406,6 @@ int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void*
     bp.q = q;
     bp.k = k;
     bp.v = v;
-    bp.o = o;
     bp.lse = lse;
     bp.d_o = d_o;
     bp.dq = dq;

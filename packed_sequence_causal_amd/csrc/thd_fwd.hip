@@ -60,6 +60,14 @@ constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
 constexpr int kWaitVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0)
 
+// 16-byte global -> LDS copy: lane i's 16 bytes land at lds + 16 * i (lds is
+// wave-uniform). Kept as a function taking a named pointer: handing the
+// builtin a pointer expression directly inside a kernel template makes the
+// host pass drop that kernel's launch stub.
+__device__ __forceinline__ void load_lds16(const char* src, char* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, 0);
+}
+
 // Position of 16-byte chunk c of LDS row r: c ^ swz(r). The XOR stays inside
 // an aligned group of 8 (or 16) chunks, so it never leaves the row.
 template <int CPR>
@@ -163,7 +171,7 @@ __global__ __launch_bounds__(kThreads, 2) void thd_fwd_kernel(FwdParams p) {
       const int r = q / S::KCPR;
       const int c = (q - r * S::KCPR) ^ swz<S::KCPR>(r);
       const char* src = kb + (size_t(rows[i]) * hkv + kvh) * S::KROWB + c * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + (wave * S::K_IPW + i) * 1024), 16, 0, 0);
+      load_lds16(src, stage + (wave * S::K_IPW + i) * 1024);
     }
 #pragma unroll
     for (int i = 0; i < S::V_IPW; ++i) {
@@ -172,7 +180,7 @@ __global__ __launch_bounds__(kThreads, 2) void thd_fwd_kernel(FwdParams p) {
       const int c = (q - r * S::VCPR) ^ swz<S::VCPR>(r);
       const int grow = S::SAME_ROWS ? rows[i] : rows[S::K_IPW + i];
       const char* src = vb + (size_t(grow) * hkv + kvh) * S::VROWB + c * 16;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(stage + S::KBYTES + (wave * S::V_IPW + i) * 1024), 16, 0, 0);
+      load_lds16(src, stage + S::KBYTES + (wave * S::V_IPW + i) * 1024);
     }
   };
 
