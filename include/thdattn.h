@@ -147,7 +147,8 @@ int thd_preferred_tiles(int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
  * meta must come from thd_build_metadata with the tile sizes of
  * thd_preferred_tiles and the current device. softmax_scale > 0 (callers
  * usually pass 1/sqrt(d_qk)). Supported (d_qk, d_v): (64,64), (128,128),
- * (192,128); Hq/Hkv <= 128. q, k, v, o, lse must be 16-byte aligned. */
+ * (192,128); Hq/Hkv <= 128. q, k, v, o, lse must be 16-byte aligned; k and v
+ * must each be smaller than 4 GiB (THD_ERANGE otherwise). */
 int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void* v,
                  void* o, float* lse, int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
                  float softmax_scale, void* hip_stream);

@@ -8,6 +8,7 @@
 // count), plus the contract version and the device of the uploaded copy.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <list>
@@ -157,6 +158,12 @@ void check_tiles(const Plan& p, int32_t group) {
   if (int64_t(p.block_t) * group > kRowsPerWg)
     fail(THD_EMISMATCH, "metadata block_t " + std::to_string(p.block_t) + " times group " +
                             std::to_string(group) + " exceeds 128 rows");
+}
+
+// The kernels address K and V with 32-bit byte offsets.
+void check_kv_bytes(int64_t total, int32_t hkv, int32_t d_qk, int32_t d_v) {
+  const int64_t row = int64_t(hkv) * 2 * std::max(d_qk, d_v);
+  if (total * row >= (int64_t(1) << 32)) fail(THD_ERANGE, "K or V exceeds 4 GiB");
 }
 
 }  // namespace
@@ -341,6 +348,7 @@ int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void*
     const DeviceMeta& d = device_meta(e);
     const int64_t n_tiles = int64_t(p.tiles.size() / 8);
     if (n_tiles * hkv >= (int64_t(1) << 31)) fail(THD_ERANGE, "grid too large");
+    check_kv_bytes(p.total, hkv, d_qk, d_v);
     FwdParams fp{};
     fp.q = q;
     fp.k = k;
@@ -398,6 +406,7 @@ int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void*
       fail(THD_EINVAL, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
                            std::to_string(need));
     const DeviceMeta& d = device_meta(e);
+    check_kv_bytes(p.total, hkv, d_qk, d_v);
     const int64_t n_tiles = int64_t(p.tiles.size() / 8);
     const int64_t n_kvtiles = int64_t(p.kvtiles.size() / 8);
     if (n_tiles * hkv >= (int64_t(1) << 31) || n_kvtiles * hkv >= (int64_t(1) << 31))

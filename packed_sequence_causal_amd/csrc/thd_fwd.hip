@@ -55,7 +55,13 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
-constexpr int kThreads = kWaves * 64;
+// Four waves of 64 lanes per workgroup, one 32-row block each, two workgroups
+// per CU: two waves share each SIMD and hide each other's latencies. (Two
+// blocks per wave at one wave per SIMD halves LDS reads per MFMA but measured
+// 1.6x slower: the latency hiding between waves matters more.)
+constexpr int kRowBlocks = 1;
+constexpr int kFwdWaves = kRowsPerWg / (32 * kRowBlocks);
+constexpr int kFwdThreads = kFwdWaves * 64;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
 constexpr int kWaitVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0)
@@ -89,13 +95,16 @@ struct FwdShape {
   static constexpr int KBYTES = BN * KROWB;       // one K tile in LDS
   static constexpr int VBYTES = BN * VROWB;
   static constexpr int STAGE = KBYTES + VBYTES;
-  static constexpr int K_IPW = BN * KCPR / 64 / kWaves;   // 1 KB loads per wave per tile
-  static constexpr int V_IPW = BN * VCPR / 64 / kWaves;
+  static constexpr int K_IPW = BN * KCPR / 64 / kFwdWaves;   // 1 KB loads per wave per tile
+  static constexpr int V_IPW = BN * VCPR / 64 / kFwdWaves;
   static constexpr bool SAME_ROWS = (KCPR == VCPR);
   static constexpr int NROWS = SAME_ROWS ? K_IPW : K_IPW + V_IPW;  // row indices per lane per tile
   static constexpr int KSTEPS = DQK / 16;
   static constexpr int DVB = DV / 32;
-  static_assert(BN * KCPR % (64 * kWaves) == 0 && BN * VCPR % (64 * kWaves) == 0,
+  static constexpr int KB = BN / 32;        // 32-key blocks per KV tile (S^T accumulators)
+  static constexpr int TS = BN / 16;        // 16-key steps of the PV product
+  static_assert(BN % 32 == 0, "KV tiles hold whole 32-key blocks");
+  static_assert(BN * KCPR % (64 * kFwdWaves) == 0 && BN * VCPR % (64 * kFwdWaves) == 0,
                 "tiles must split into whole 1 KB loads per wave");
   static_assert(DQK % 16 == 0 && DV % 32 == 0, "head dims must suit the MFMA tiles");
   static_assert(KCPR == 8 || KCPR == 16 || KCPR == 24, "chunk swizzle needs 8, 16 or 24 chunks");
@@ -103,10 +112,17 @@ struct FwdShape {
 };
 
 template <int DQK, int DV>
-__global__ __launch_bounds__(kThreads, 2) void thd_fwd_kernel(FwdParams p) {
+__global__ __launch_bounds__(kFwdThreads, 2) void thd_fwd_kernel(FwdParams p) {
   using S = FwdShape<DQK, DV>;
   constexpr int BN = S::BN;
-  __shared__ __attribute__((aligned(1024))) char smem[2 * S::STAGE];
+  constexpr int RB = kRowBlocks;
+  // The two ring stages are separate arrays, and the tile loop is unrolled by
+  // two so that each step names its stages statically: the compiler can then
+  // tell that the transpose reads of one stage do not alias the in-flight LDS
+  // writes into the other, and does not wait for the next tile's loads before
+  // reading the current one.
+  __shared__ __attribute__((aligned(1024))) char smem0[S::STAGE];
+  __shared__ __attribute__((aligned(1024))) char smem1[S::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -125,13 +141,21 @@ __global__ __launch_bounds__(kThreads, 2) void thd_fwd_kernel(FwdParams p) {
   const int n_full = td[7];
   const int key_last = q_glob0 + n_rows - 1;   // keys past this are seen by no row
 
+  // Row block rb of this wave holds rows 32 * (RB * wave + rb) + lane % 32.
   const int G = p.group;
-  const int row = wave * 32 + lrow;
-  const int tok = row / G;
-  const int head = kvh * G + (row - tok * G);
-  const bool valid = tok < n_rows;
-  const int qpos = valid ? q_glob0 + tok : INT_MAX;
-  const bool wave_active = (wave * 32) / G < n_rows;
+  int tok[RB], head[RB], qpos[RB];
+  bool valid[RB], rb_active[RB];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const int row0 = 32 * (RB * wave + rb);
+    const int row = row0 + lrow;
+    tok[rb] = row / G;
+    head[rb] = kvh * G + (row - tok[rb] * G);
+    valid[rb] = tok[rb] < n_rows;
+    qpos[rb] = valid[rb] ? q_glob0 + tok[rb] : INT_MAX;
+    rb_active[rb] = row0 / G < n_rows;          // wave-uniform
+  }
+  const bool wave_active = rb_active[0];
 
   const __bf16* __restrict__ qp = static_cast<const __bf16*>(p.q);
   const char* __restrict__ kb = static_cast<const char*>(p.k);
@@ -140,46 +164,56 @@ __global__ __launch_bounds__(kThreads, 2) void thd_fwd_kernel(FwdParams p) {
   const int hkv = p.hkv;
 
   // Q^T operand: lane holds Q[row][16*st + 8*half .. +7] for each k-step.
-  bf16x8 qf[S::KSTEPS];
-  {
-    const __bf16* qrow = qp + (size_t(q_local0 + tok) * p.hq + head) * DQK + 8 * half;
+  bf16x8 qf[RB][S::KSTEPS];
+#pragma unroll
+  for (int rb = 0; rb < RB; ++rb) {
+    const __bf16* qrow = qp + (size_t(q_local0 + tok[rb]) * p.hq + head[rb]) * DQK + 8 * half;
 #pragma unroll
     for (int st = 0; st < S::KSTEPS; ++st)
-      qf[st] = valid ? *reinterpret_cast<const bf16x8*>(qrow + 16 * st) : bf16x8{};
+      qf[rb][st] = valid[rb] ? *reinterpret_cast<const bf16x8*>(qrow + 16 * st) : bf16x8{};
   }
 
   // Loader geometry: load i of this wave fills LDS bytes [1 KB * gi, +1 KB) of
   // the K (or V) tile, gi = wave * IPW + i; lane l writes slot q = 64 gi + l,
   // i.e. row q / CPR, chunk position q % CPR, holding global chunk
-  // (q % CPR) ^ swz(row).
+  // (q % CPR) ^ swz(row). Everything but the gathered row is the same for
+  // every tile, so each load's byte offset is precomputed once per lane; K
+  // and V are below 4 GiB (checked at the boundary), so offsets are 32-bit.
+  int key_rel[S::NROWS];      // tile-relative key of this lane's load i
+  uint32_t lane_off[S::K_IPW + S::V_IPW];
+#pragma unroll
+  for (int i = 0; i < S::K_IPW; ++i) {
+    const int q = (wave * S::K_IPW + i) * 64 + lane;
+    const int r = q / S::KCPR;
+    key_rel[i] = r;
+    lane_off[i] = uint32_t(kvh * S::KROWB + (((q - r * S::KCPR) ^ swz<S::KCPR>(r)) << 4));
+  }
+#pragma unroll
+  for (int i = 0; i < S::V_IPW; ++i) {
+    const int q = (wave * S::V_IPW + i) * 64 + lane;
+    const int r = q / S::VCPR;
+    if (!S::SAME_ROWS) key_rel[S::K_IPW + i] = r;
+    lane_off[S::K_IPW + i] = uint32_t(kvh * S::VROWB + (((q - r * S::VCPR) ^ swz<S::VCPR>(r)) << 4));
+  }
+  const uint32_t k_stride = uint32_t(hkv * S::KROWB);   // bytes per gathered K row
+  const uint32_t v_stride = uint32_t(hkv * S::VROWB);
   int rows_cur[S::NROWS];   // gathered rows of this lane's keys, next tile to load
   int rows_nxt[S::NROWS];   // ... and the tile after it
-  auto key_row = [&](int i) -> int {   // tile-relative row of this lane's load i
-    if (i < S::K_IPW) return ((wave * S::K_IPW + i) * 64 + lane) / S::KCPR;
-    return ((wave * S::V_IPW + (i - S::K_IPW)) * 64 + lane) / S::VCPR;
-  };
   auto fetch_rows = [&](int j, int* rows) {
     const int key0 = kv_start + j * BN;
 #pragma unroll
-    for (int i = 0; i < S::NROWS; ++i) rows[i] = kv_row[min(key0 + key_row(i), key_last)];
+    for (int i = 0; i < S::NROWS; ++i) rows[i] = kv_row[min(key0 + key_rel[i], key_last)];
   };
-  auto issue_tile = [&](int j, const int* rows) {
-    char* stage = smem + (j & 1) * S::STAGE;
+  auto issue_tile = [&](char* stage, const int* rows) {
 #pragma unroll
     for (int i = 0; i < S::K_IPW; ++i) {
-      const int q = (wave * S::K_IPW + i) * 64 + lane;
-      const int r = q / S::KCPR;
-      const int c = (q - r * S::KCPR) ^ swz<S::KCPR>(r);
-      const char* src = kb + (size_t(rows[i]) * hkv + kvh) * S::KROWB + c * 16;
+      const char* src = kb + (uint32_t(rows[i]) * k_stride + lane_off[i]);
       load_lds16(src, stage + (wave * S::K_IPW + i) * 1024);
     }
 #pragma unroll
     for (int i = 0; i < S::V_IPW; ++i) {
-      const int q = (wave * S::V_IPW + i) * 64 + lane;
-      const int r = q / S::VCPR;
-      const int c = (q - r * S::VCPR) ^ swz<S::VCPR>(r);
       const int grow = S::SAME_ROWS ? rows[i] : rows[S::K_IPW + i];
-      const char* src = vb + (size_t(grow) * hkv + kvh) * S::VROWB + c * 16;
+      const char* src = vb + (uint32_t(grow) * v_stride + lane_off[S::K_IPW + i]);
       load_lds16(src, stage + S::KBYTES + (wave * S::V_IPW + i) * 1024);
     }
   };
@@ -194,85 +228,100 @@ __global__ __launch_bounds__(kThreads, 2) void thd_fwd_kernel(FwdParams p) {
   const int tr_c = lane & 3;
   const int tr_dv = 16 * ((lane >> 4) & 1) + 4 * tr_c;     // plus 32*b
 
-  f32x16 acc[S::DVB];
+  f32x16 acc[RB][S::DVB];
+  float m_run[RB], l_run[RB];   // running max of scale*log2(e)*s, and this lane's share of the sum
 #pragma unroll
-  for (int b = 0; b < S::DVB; ++b) acc[b] = f32x16{};
-  float m_run = -INFINITY;   // running max of scale*log2(e)*s for this lane's row
-  float l_run = 0.0f;        // this lane's share of the row's sum of 2^(...)
+  for (int rb = 0; rb < RB; ++rb) {
+#pragma unroll
+    for (int b = 0; b < S::DVB; ++b) acc[rb][b] = f32x16{};
+    m_run[rb] = -INFINITY;
+    l_run[rb] = 0.0f;
+  }
   const float c2 = p.scale_log2;
 
   // Prologue: rows of tiles 0 and 1, then tile 0's data.
   fetch_rows(0, rows_cur);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  issue_tile(0, rows_cur);
+  issue_tile(smem0, rows_cur);
   if (n_kv > 1) fetch_rows(1, rows_cur);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
 
-  for (int j = 0; j < n_kv; ++j) {
-    // Stage j&1 holds tile j; rows_cur holds tile j+1's rows.
-    if (j + 1 < n_kv) issue_tile(j + 1, rows_cur);
+  auto step = [&](int j, const char* stage, char* next) {
+    // stage holds tile j; rows_cur holds tile j+1's rows.
+    if (j + 1 < n_kv) issue_tile(next, rows_cur);
     if (j + 2 < n_kv) fetch_rows(j + 2, rows_nxt);
-    const char* stage = smem + (j & 1) * S::STAGE;
 
     if (wave_active) {
-      // S^T = K Q^T for keys [32*kb, 32*kb + 32) of the tile.
-      f32x16 s[2] = {f32x16{}, f32x16{}};
+      // S^T = K Q^T for keys [32*kb, 32*kb + 32) of the tile; each K fragment
+      // read from LDS feeds every row block.
+      f32x16 s[RB][S::KB];
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+#pragma unroll
+        for (int kb2 = 0; kb2 < S::KB; ++kb2) s[rb][kb2] = f32x16{};
 #pragma unroll
       for (int st = 0; st < S::KSTEPS; ++st) {
         const int cpos = ((2 * st + half) ^ k_swz) * 16;
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
+        for (int kb2 = 0; kb2 < S::KB; ++kb2) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + k_off + 32 * kb2 * S::KROWB + cpos);
-          s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb2], 0, 0, 0);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            if (rb_active[rb]) s[rb][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][st], s[rb][kb2], 0, 0, 0);
         }
       }
 
-      if (j >= n_full) {
-        const int key0 = kv_start + j * BN + 4 * half;
+      bf16x8 pb[RB][S::TS];
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int rb = 0; rb < RB; ++rb) {
+        if (!rb_active[rb]) continue;
+        if (j >= n_full) {
+          const int key0 = kv_start + j * BN + 4 * half;
+#pragma unroll
+          for (int kb2 = 0; kb2 < S::KB; ++kb2)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int key = key0 + 32 * kb2 + 8 * (r >> 2) + (r & 3);
+              if (key > qpos[rb]) s[rb][kb2][r] = -INFINITY;
+            }
+        }
+
+        float mx = s[rb][0][0];
+#pragma unroll
+        for (int kb2 = 0; kb2 < S::KB; ++kb2)
+#pragma unroll
+          for (int r = (kb2 == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[rb][kb2][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // Each row decides on its own (so a row's arithmetic never depends on
+        // its neighbours); the wave only skips the rescale when no row needs it.
+        const float m_tile = mx * c2;
+        const bool need = m_tile > m_run[rb] + kRescaleSlack;
+        if (__any(need)) {
+          const float alpha = need ? __builtin_amdgcn_exp2f(m_run[rb] - m_tile) : 1.0f;
+#pragma unroll
+          for (int b = 0; b < S::DVB; ++b)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[rb][b][r] *= alpha;
+          l_run[rb] *= alpha;
+          m_run[rb] = need ? m_tile : m_run[rb];
+        }
+
+        const float neg_m = -m_run[rb];
+#pragma unroll
+        for (int kb2 = 0; kb2 < S::KB; ++kb2)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
-            const int key = key0 + 32 * kb2 + 8 * (r >> 2) + (r & 3);
-            if (key > qpos) s[kb2][r] = -INFINITY;
+            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][kb2][r], c2, neg_m));
+            l_run[rb] += e;
+            pb[rb][2 * kb2 + (r >> 3)][r & 7] = static_cast<__bf16>(e);
           }
       }
 
-      float mx = s[0][0];
+      // O^T += V^T P^T, 16 keys per MFMA: keys 16t + 4*half + {0..3, 8..11};
+      // each V^T fragment feeds every row block.
 #pragma unroll
-      for (int r = 1; r < 16; ++r) mx = fmaxf(mx, s[0][r]);
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[1][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      // Each row decides on its own (so a row's arithmetic never depends on
-      // its neighbours); the wave only skips the rescale when no row needs it.
-      const float m_tile = mx * c2;
-      const bool need = m_tile > m_run + kRescaleSlack;
-      if (__any(need)) {
-        const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_tile) : 1.0f;
-#pragma unroll
-        for (int b = 0; b < S::DVB; ++b)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) acc[b][r] *= alpha;
-        l_run *= alpha;
-        m_run = need ? m_tile : m_run;
-      }
-
-      const float neg_m = -m_run;
-      bf16x8 pb[4];
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r], c2, neg_m));
-          l_run += e;
-          pb[2 * kb2 + (r >> 3)][r & 7] = static_cast<__bf16>(e);
-        }
-
-      // O^T += V^T P^T, 16 keys per MFMA: keys 16t + 4*half + {0..3, 8..11}.
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
+      for (int t = 0; t < S::TS; ++t) {
         const int r0 = 16 * t + 4 * half + tr_a;
         const int r1 = r0 + 8;
 #pragma unroll
@@ -283,40 +332,50 @@ __global__ __launch_bounds__(kThreads, 2) void thd_fwd_kernel(FwdParams p) {
           const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + off0));
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + off1));
           const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[t], acc[b], 0, 0, 0);
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb)
+            if (rb_active[rb]) acc[rb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[rb][t], acc[rb][b], 0, 0, 0);
         }
       }
     }
 
     // Tile j+1 (and tile j+2's rows) must have landed, and every wave must be
-    // done with stage j&1 before it is refilled.
+    // done with this stage before it is refilled.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     __syncthreads();
 #pragma unroll
     for (int i = 0; i < S::NROWS; ++i) rows_cur[i] = rows_nxt[i];
+  };
+  for (int j = 0; j < n_kv; j += 2) {
+    step(j, smem0, smem1);
+    if (j + 1 < n_kv) step(j + 1, smem1, smem0);
   }
 
-  if (!wave_active) return;
-  const float l_tot = l_run + __shfl_xor(l_run, 32);
-  if (!valid) return;
-  const float inv = 1.0f / l_tot;
-  __bf16* orow = static_cast<__bf16*>(p.o) + (size_t(q_local0 + tok) * p.hq + head) * DV;
 #pragma unroll
-  for (int b = 0; b < S::DVB; ++b)
+  for (int rb = 0; rb < RB; ++rb) {
+    if (!rb_active[rb]) continue;
+    const float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 32);
+    if (!valid[rb]) continue;
+    const float inv = 1.0f / l_tot;
+    __bf16* orow = static_cast<__bf16*>(p.o) + (size_t(q_local0 + tok[rb]) * p.hq + head[rb]) * DV;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      bf16x4 out;
+    for (int b = 0; b < S::DVB; ++b)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) out[e] = static_cast<__bf16>(acc[b][4 * g + e] * inv);
-      *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * g + 4 * half) = out;
-    }
-  if (half == 0) p.lse[size_t(q_local0 + tok) * p.hq + head] = (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = static_cast<__bf16>(acc[rb][b][4 * g + e] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * g + 4 * half) = out;
+      }
+    if (half == 0)
+      p.lse[size_t(q_local0 + tok[rb]) * p.hq + head[rb]] = (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
+  }
 }
 
 template <int DQK, int DV>
 int launch(const FwdParams& p, void* stream) {
   const dim3 grid(unsigned(int64_t(p.n_tiles) * p.hkv));
-  hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV>), grid, dim3(kThreads), 0,
+  hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV>), grid, dim3(kFwdThreads), 0,
                      static_cast<hipStream_t>(stream), p);
   return int(hipGetLastError());
 }
