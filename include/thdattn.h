@@ -61,8 +61,8 @@ typedef enum {
   THD_EUNSUPPORTED = -8   /* no kernel for these head dims or group size */
 } thd_status;
 
-/* Version of the tile-table contract (the per-tile bounds below). */
-#define THD_META_VERSION 1
+/* Version of the tile-table contract (the per-tile bounds and work items below). */
+#define THD_META_VERSION 2
 
 /* Fields of a metadata object, for thd_meta_copy. All int32.
  *   Q_GLOBAL  [T_local]       global packed position of each local query row
@@ -78,14 +78,27 @@ typedef enum {
  *   KVTILES   [n_kvtiles*8]   per key tile (backward; together they cover
  *                             every key once): doc, kv_global_start, n_keys,
  *                             q_tile_begin, q_tile_end (the query tiles that
- *                             see the tile, empty for unseen keys), 0, 0, 0 */
+ *                             see the tile, empty for unseen keys), 0, 0, 0
+ *   ITEMS     [n_items*4]     forward work items, longest first: tile,
+ *                             kv_tile_begin, kv_tile_end, part slot (-1 when
+ *                             the tile is not split)
+ *   SPLITS    [n_splits*4]    tiles whose key range is split: tile, first part
+ *                             slot, number of parts, 0
+ * With concurrency C > 0 (work items of one kv head the device runs at once)
+ * and fewer than 2C tiles, the key range of tiles longer than
+ * kv_split = max(ceil(sum of n_kv_tiles / C), 8) KV tiles is cut into
+ * min(ceil(n_kv_tiles / kv_split), n_full_kv_tiles) near-equal parts, every
+ * part starting with a KV tile its rows see whole; the forward merges the
+ * parts' partial results. */
 enum {
   THD_FIELD_Q_GLOBAL = 0,
   THD_FIELD_KV_ROW = 1,
   THD_FIELD_CHUNK_OFF = 2,
   THD_FIELD_TILES = 3,
   THD_FIELD_ORDER = 4,
-  THD_FIELD_KVTILES = 5
+  THD_FIELD_KVTILES = 5,
+  THD_FIELD_ITEMS = 6,
+  THD_FIELD_SPLITS = 7
 };
 
 typedef struct thd_meta thd_meta;   /* opaque, library-owned, reference-counted */
@@ -97,6 +110,10 @@ typedef struct {
   int64_t n_kvtiles;
   int64_t useful_pairs;     /* visible (local query, key) pairs: sum L_i (L_i + 1) / (2cp) */
   int64_t max_kv_tiles;     /* largest n_kv_tiles of any tile */
+  int64_t n_items;          /* forward work items */
+  int64_t n_splits;         /* tiles whose key range is split */
+  int64_t n_part_slots;     /* partial-result slots (sum of parts over split tiles) */
+  int32_t concurrency, kv_split;
   int32_t n_docs, cp, rank, block_t, block_n, version;
   int32_t device;           /* device holding the uploaded copy, -1 = host only */
   int32_t cache_hit;        /* 1 if this handle came from the cache */
@@ -116,13 +133,16 @@ int thd_plan_partition(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32
 
 /* Build (or fetch from the cache) the metadata of one rank's attention: the
  * partition maps, per-tile document/causal bounds for block_t query tokens by
- * block_n keys, the largest-first tile order and the backward key tiles.
- * device >= 0 also uploads the arrays to that device (once per cache entry);
- * device = -1 builds host arrays only. The cache key holds every input
- * (all lengths, cp, rank, block sizes, contract version, device).
- * On success *out is a new reference: release it with thd_meta_release. */
+ * block_n keys, the largest-first tile order, the forward work items (see
+ * THD_FIELD_ITEMS; concurrency >= 0, 0 = never split a tile) and the backward
+ * key tiles. device >= 0 also uploads the arrays to that device (once per
+ * cache entry); device = -1 builds host arrays only. The cache key holds every
+ * input (all lengths, cp, rank, block sizes, concurrency, contract version,
+ * device). On success *out is a new reference: release it with
+ * thd_meta_release. */
 int thd_build_metadata(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank,
-                       int32_t block_t, int32_t block_n, int32_t device, thd_meta** out);
+                       int32_t block_t, int32_t block_n, int32_t concurrency, int32_t device,
+                       thd_meta** out);
 
 int thd_meta_info(const thd_meta* meta, thd_meta_info_t* info);
 
@@ -143,15 +163,23 @@ int thd_cache_clear(void);
 int thd_preferred_tiles(int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
                         int32_t* block_t, int32_t* block_n);
 
+/* Bytes of device workspace thd_attn_fwd needs for the partial results of
+ * split tiles (0 when no tile is split). */
+int thd_attn_fwd_workspace(const thd_meta* meta, int32_t hq, int32_t hkv, int32_t d_v,
+                           int64_t* bytes);
+
 /* Forward: o and lse for every local query row and q head.
  * meta must come from thd_build_metadata with the tile sizes of
  * thd_preferred_tiles and the current device. softmax_scale > 0 (callers
  * usually pass 1/sqrt(d_qk)). Supported (d_qk, d_v): (64,64), (128,128),
  * (192,128); Hq/Hkv <= 128. q, k, v, o, lse must be 16-byte aligned; k and v
- * must each be smaller than 4 GiB (THD_ERANGE otherwise). */
+ * must each be smaller than 4 GiB (THD_ERANGE otherwise). workspace (16-byte
+ * aligned, at least thd_attn_fwd_workspace bytes; may be NULL when that is 0)
+ * holds the split tiles' partial results; the forward allocates nothing. */
 int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void* v,
                  void* o, float* lse, int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
-                 float softmax_scale, void* hip_stream);
+                 float softmax_scale, void* workspace, int64_t workspace_bytes,
+                 void* hip_stream);
 
 /* Bytes of device workspace thd_attn_bwd needs (caller allocates). */
 int thd_attn_bwd_workspace(const thd_meta* meta, int32_t hq, int64_t* bytes);

@@ -5,8 +5,8 @@ Test infrastructure only (see the package docstring).
 The subject page ("kvallgather cp thd load balance", section "What this PR does
 / why we need it?") says metadata is cached to avoid repeated computation but
 gives no format. The format below is this project's interface contract between
-the host planner and the GPU kernels (version 1). It is unique given
-(lengths, cp, rank, BT, BN), so the host library must reproduce it bit for bit.
+the host planner and the GPU kernels (version 2). It is unique given
+(lengths, cp, rank, BT, BN, concurrency), so the host library must reproduce it bit for bit.
 
 Definitions (all integer, floor division of non-negative values):
 
@@ -23,6 +23,22 @@ KV tile j of a Q tile covers keys [cu_i + j*BN, cu_i + min((j+1)*BN, kv_len)).
 order[n_tiles]: tile indices sorted by n_kv descending, ties by index
 ascending (largest work first). Parity unpinned: it is a scheduling choice with
 no truth outside this definition.
+
+Forward work items (key-range splitting for load balance). Given
+concurrency C (work items of one kv head the device runs at once; 0 = never
+split) and T_kv = sum of n_kv over the tiles:
+    kv_split = 0                            if C <= 0 or n_tiles >= 2 C
+             = max(ceil(T_kv / C), 8)       otherwise
+A tile with kv_split > 0, n_kv > kv_split and n_full >= 2 is cut into
+P = min(ceil(n_kv / kv_split), n_full) parts at s_i = floor(i n_kv / P),
+i = 1..P-1, then clamped from the last one down: s_{P-1} <= n_full - 1 and
+s_i <= s_{i+1} - 1. Part i covers KV tiles [s_i, s_{i+1}) (s_0 = 0,
+s_P = n_kv), so every part starts with a KV tile all of its rows see whole.
+items[n_items][4] = [tile, kv_begin, kv_end, part slot or -1], listed by tile
+then part and sorted by kv_end - kv_begin descending (ties by that listing
+order); part slots count up over the split tiles in tile order.
+splits[n_split][4] = [tile, first part slot, P, 0] in tile order.
+(The items' order, like order above, is parity unpinned.)
 
 kvtiles[m][8] (backward): for document i, j = 0 .. ceil(L_i / BN) - 1:
     ks      = cu_i + j*BN
@@ -41,7 +57,7 @@ import numpy as np
 
 from . import partition
 
-VERSION = 1
+VERSION = 2
 TILE_FIELDS = ("q_local_start", "q_global_start", "n_rows", "doc", "slot",
                "kv_start", "n_kv_tiles", "n_full_kv_tiles")
 KVTILE_FIELDS = ("doc", "kv_global_start", "n_keys", "q_tile_begin", "q_tile_end",
@@ -109,3 +125,43 @@ def useful_pairs_closed_form(seqlens, cp: int) -> int:
         length = int(length)
         total += length * (length + 1) // (2 * cp)
     return total
+
+
+def kv_split_for(tile_table: np.ndarray, concurrency: int) -> int:
+    n_tiles = int(tile_table.shape[0])
+    if concurrency <= 0 or n_tiles >= 2 * concurrency:
+        return 0
+    total = sum(int(x) for x in tile_table[:, 6])
+    return max(_ceil_div(total, concurrency), 8)
+
+
+def _parts(n_kv: int, n_full: int, kv_split: int):
+    if kv_split <= 0 or n_kv <= kv_split or n_full < 2:
+        return [(0, n_kv)]
+    count = min(_ceil_div(n_kv, kv_split), n_full)
+    cuts = [i * n_kv // count for i in range(1, count)]
+    cuts[-1] = min(cuts[-1], n_full - 1)
+    for i in range(len(cuts) - 2, -1, -1):
+        cuts[i] = min(cuts[i], cuts[i + 1] - 1)
+    bounds = [0] + cuts + [n_kv]
+    return [(bounds[i], bounds[i + 1]) for i in range(count)]
+
+
+def items_and_splits(tile_table: np.ndarray, concurrency: int):
+    """(items [n_items][4] in work order, splits [n_split][4])."""
+    kv_split = kv_split_for(tile_table, concurrency)
+    natural = []
+    splits = []
+    slot = 0
+    for t in range(tile_table.shape[0]):
+        parts = _parts(int(tile_table[t, 6]), int(tile_table[t, 7]), kv_split)
+        if len(parts) == 1:
+            natural.append([t, parts[0][0], parts[0][1], -1])
+            continue
+        splits.append([t, slot, len(parts), 0])
+        for begin, end in parts:
+            natural.append([t, begin, end, slot])
+            slot += 1
+    ranked = sorted(range(len(natural)), key=lambda i: (-(natural[i][2] - natural[i][1]), i))
+    items = np.asarray([natural[i] for i in ranked], dtype=np.int32).reshape(-1, 4)
+    return items, np.asarray(splits, dtype=np.int32).reshape(-1, 4)

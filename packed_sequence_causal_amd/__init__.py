@@ -26,8 +26,9 @@ STATUS_NAMES = {
     -1: "THD_EINVAL", -2: "THD_ENOTDIV", -3: "THD_ERANGE", -4: "THD_EALIGN",
     -5: "THD_EMISMATCH", -6: "THD_EHIP", -7: "THD_ENOMEM", -8: "THD_EUNSUPPORTED",
 }
-FIELDS = {"q_global": 0, "kv_row": 1, "chunk_off": 2, "tiles": 3, "order": 4, "kvtiles": 5}
-META_VERSION = 1
+FIELDS = {"q_global": 0, "kv_row": 1, "chunk_off": 2, "tiles": 3, "order": 4, "kvtiles": 5,
+          "items": 6, "splits": 7}
+META_VERSION = 2
 
 
 class ThdError(RuntimeError):
@@ -44,6 +45,8 @@ class _Info(ctypes.Structure):
         ("total_tokens", ctypes.c_int64), ("local_tokens", ctypes.c_int64),
         ("n_tiles", ctypes.c_int64), ("n_kvtiles", ctypes.c_int64),
         ("useful_pairs", ctypes.c_int64), ("max_kv_tiles", ctypes.c_int64),
+        ("n_items", ctypes.c_int64), ("n_splits", ctypes.c_int64), ("n_part_slots", ctypes.c_int64),
+        ("concurrency", ctypes.c_int32), ("kv_split", ctypes.c_int32),
         ("n_docs", ctypes.c_int32), ("cp", ctypes.c_int32), ("rank", ctypes.c_int32),
         ("block_t", ctypes.c_int32), ("block_n", ctypes.c_int32), ("version", ctypes.c_int32),
         ("device", ctypes.c_int32), ("cache_hit", ctypes.c_int32),
@@ -62,14 +65,17 @@ def _load():
     sigs = {
         "thd_last_error": (ctypes.c_char_p, []),
         "thd_plan_partition": (ctypes.c_int, [pi32, i32, i32, i32, pi64, pi64, pi32, pi32, pi32]),
-        "thd_build_metadata": (ctypes.c_int, [pi32, i32, i32, i32, i32, i32, i32, ctypes.POINTER(p)]),
+        "thd_build_metadata": (ctypes.c_int, [pi32, i32, i32, i32, i32, i32, i32, i32,
+                                              ctypes.POINTER(p)]),
         "thd_meta_info": (ctypes.c_int, [p, ctypes.POINTER(_Info)]),
         "thd_meta_copy": (ctypes.c_int, [p, i32, pi32, i64]),
         "thd_meta_release": (None, [p]),
         "thd_cache_stats": (ctypes.c_int, [pi64, pi64, pi64, pi64]),
         "thd_cache_clear": (ctypes.c_int, []),
         "thd_preferred_tiles": (ctypes.c_int, [i32, i32, i32, i32, pi32, pi32]),
-        "thd_attn_fwd": (ctypes.c_int, [p, p, p, p, p, p, i32, i32, i32, i32, ctypes.c_float, p]),
+        "thd_attn_fwd_workspace": (ctypes.c_int, [p, i32, i32, i32, pi64]),
+        "thd_attn_fwd": (ctypes.c_int, [p, p, p, p, p, p, i32, i32, i32, i32, ctypes.c_float, p, i64,
+                                        p]),
         "thd_attn_bwd_workspace": (ctypes.c_int, [p, i32, pi64]),
         "thd_attn_bwd": (ctypes.c_int, [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
                                         ctypes.c_float, p, i64, p]),
@@ -84,7 +90,8 @@ def _load():
 _lib = _load()
 EXPORTS = ("thd_last_error", "thd_plan_partition", "thd_build_metadata", "thd_meta_info",
            "thd_meta_copy", "thd_meta_release", "thd_cache_stats", "thd_cache_clear",
-           "thd_preferred_tiles", "thd_attn_fwd", "thd_attn_bwd_workspace", "thd_attn_bwd")
+           "thd_preferred_tiles", "thd_attn_fwd_workspace", "thd_attn_fwd",
+           "thd_attn_bwd_workspace", "thd_attn_bwd")
 
 
 def _check(code: int):
@@ -139,11 +146,14 @@ class Meta:
         inf = self.info()
         n = {"q_global": inf["local_tokens"], "kv_row": inf["total_tokens"],
              "chunk_off": inf["n_docs"] * 2 * inf["cp"], "tiles": inf["n_tiles"] * 8,
-             "order": inf["n_tiles"], "kvtiles": inf["n_kvtiles"] * 8}[name]
+             "order": inf["n_tiles"], "kvtiles": inf["n_kvtiles"] * 8,
+             "items": inf["n_items"] * 4, "splits": inf["n_splits"] * 4}[name]
         out = np.empty(n, np.int32)
         _check(_lib.thd_meta_copy(self._h, FIELDS[name], _ptr32(out), n))
         if name in ("tiles", "kvtiles"):
             out = out.reshape(-1, 8)
+        if name in ("items", "splits"):
+            out = out.reshape(-1, 4)
         return out
 
     def release(self):
@@ -159,12 +169,15 @@ class Meta:
 
 
 def build_metadata(*, seqlens, cp: int, rank: int, block_t: int, block_n: int,
-                   device: int = -1) -> Meta:
-    """Build or fetch cached metadata; device >= 0 also uploads it there."""
+                   concurrency: int = 0, device: int = -1) -> Meta:
+    """Build or fetch cached metadata; device >= 0 also uploads it there.
+
+    concurrency: work items of one kv head the device runs at once (0 = never
+    split a tile's key range)."""
     lens = _lengths(seqlens)
     h = ctypes.c_void_p()
-    _check(_lib.thd_build_metadata(_ptr32(lens), len(lens), cp, rank, block_t, block_n, device,
-                                   ctypes.byref(h)))
+    _check(_lib.thd_build_metadata(_ptr32(lens), len(lens), cp, rank, block_t, block_n,
+                                   concurrency, device, ctypes.byref(h)))
     return Meta(h)
 
 
@@ -196,14 +209,40 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+_CUS = {}
+_WORKSPACE = {}
+FWD_WORKGROUPS_PER_CU = 2   # the forward kernel's occupancy (LDS and registers)
+
+
+def device_concurrency(device: int, hkv: int) -> int:
+    """Forward work items of one kv head the device runs at once."""
+    if device not in _CUS:
+        _CUS[device] = _torch().cuda.get_device_properties(device).multi_processor_count
+    return max(1, _CUS[device] * FWD_WORKGROUPS_PER_CU // hkv)
+
+
 def device_metadata(*, seqlens, cp: int, rank: int, hq: int, hkv: int, d_qk: int, d_v: int,
-                    device: int) -> Meta:
+                    device: int, concurrency: int | None = None) -> Meta:
     bt, bn = preferred_tiles(hq=hq, hkv=hkv, d_qk=d_qk, d_v=d_v)
-    return build_metadata(seqlens=seqlens, cp=cp, rank=rank, block_t=bt, block_n=bn, device=device)
+    if concurrency is None:
+        concurrency = device_concurrency(device, hkv)
+    return build_metadata(seqlens=seqlens, cp=cp, rank=rank, block_t=bt, block_n=bn,
+                          concurrency=concurrency, device=device)
+
+
+def _workspace(device, nbytes: int):
+    """A cached device buffer of at least nbytes (None for 0)."""
+    if nbytes <= 0:
+        return None
+    buf = _WORKSPACE.get(device)
+    if buf is None or buf.numel() < nbytes:
+        buf = _torch().empty(nbytes, dtype=_torch().uint8, device=device)
+        _WORKSPACE[device] = buf
+    return buf
 
 
 def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=None, lse=None,
-             stream=None, meta: Meta | None = None):
+             stream=None, meta: Meta | None = None, concurrency: int | None = None):
     """Forward attention for one rank. Returns (o bf16 [T_loc,Hq,dv], lse fp32 [T_loc,Hq]).
 
     q [T_loc, Hq, dqk], k [T, Hkv, dqk], v [T, Hkv, dv]: bf16 CUDA tensors,
@@ -217,11 +256,14 @@ def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=No
     device = q.device.index
     if meta is None:
         meta = device_metadata(seqlens=seqlens, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=d_qk,
-                               d_v=d_v, device=device)
+                               d_v=d_v, device=device, concurrency=concurrency)
     inf = meta.info()
     if q.shape[0] != inf["local_tokens"] or k.shape[0] != inf["total_tokens"] \
             or v.shape[0] != inf["total_tokens"]:
         raise ThdError(-5, "token counts do not match the lengths")
+    need = ctypes.c_int64()
+    _check(_lib.thd_attn_fwd_workspace(meta.handle, hq, hkv, d_v, ctypes.byref(need)))
+    ws = _workspace(q.device, need.value)
     if out is None:
         out = torch.empty((q.shape[0], hq, d_v), dtype=torch.bfloat16, device=q.device)
     if lse is None:
@@ -229,6 +271,7 @@ def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=No
     scale = 1.0 / math.sqrt(d_qk) if softmax_scale is None else float(softmax_scale)
     _check(_lib.thd_attn_fwd(meta.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                              out.data_ptr(), lse.data_ptr(), hq, hkv, d_qk, d_v, scale,
+                             None if ws is None else ws.data_ptr(), need.value,
                              _stream_handle(stream, q.device)))
     return out, lse
 

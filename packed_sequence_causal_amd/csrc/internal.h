@@ -23,9 +23,9 @@ struct Error {
 // Field meanings are documented with THD_FIELD_* in thdattn.h.
 struct Plan {
   std::vector<int32_t> seqlens;
-  int32_t cp = 1, rank = 0, block_t = 1, block_n = 1;
-  int64_t total = 0, local = 0, useful_pairs = 0, max_kv_tiles = 0;
-  std::vector<int32_t> q_global, kv_row, chunk_off, tiles, order, kvtiles;
+  int32_t cp = 1, rank = 0, block_t = 1, block_n = 1, concurrency = 0, kv_split = 0;
+  int64_t total = 0, local = 0, useful_pairs = 0, max_kv_tiles = 0, n_part_slots = 0;
+  std::vector<int32_t> q_global, kv_row, chunk_off, tiles, order, kvtiles, items, splits;
 };
 
 // Checks lengths/cp/rank; throws Error. Returns T.
@@ -37,7 +37,8 @@ void plan_partition(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t 
 
 // Builds the full plan (partition maps + tile tables).
 std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t cp,
-                                 int32_t rank, int32_t block_t, int32_t block_n);
+                                 int32_t rank, int32_t block_t, int32_t block_n,
+                                 int32_t concurrency);
 
 // Device copies of the arrays the kernels read.
 struct DeviceMeta {
@@ -48,6 +49,8 @@ struct DeviceMeta {
   const int32_t* order = nullptr;
   const int32_t* kvtiles = nullptr;
   const int32_t* q_global = nullptr;
+  const int32_t* items = nullptr;
+  const int32_t* splits = nullptr;
 };
 
 struct MetaEntry {
@@ -78,13 +81,28 @@ struct FwdParams {
   const void* v;
   void* o;
   float* lse;
+  float* partial;     // workspace: per (part slot, kv head) O rows (fp32) then their lse
   const int32_t* tiles;
-  const int32_t* order;
+  const int32_t* items;
+  const int32_t* splits;
   const int32_t* kv_row;
-  int32_t n_tiles, hq, hkv, group, block_t;
+  int32_t n_items, n_splits, hq, hkv, group, block_t;
   int64_t total;
   float scale_log2;   // softmax_scale * log2(e)
 };
+
+#if defined(__HIPCC__)
+#define THD_HOST_DEVICE __host__ __device__
+#else
+#define THD_HOST_DEVICE
+#endif
+
+// Floats of forward workspace per (part slot, kv head): the part's O rows
+// (rows * d_v) then its per-row log2-sum-exp (rows), padded to a multiple of 4
+// so every slot starts 16-byte aligned.
+THD_HOST_DEVICE inline int64_t fwd_partial_floats(int32_t block_t, int32_t group, int32_t d_v) {
+  return (int64_t(block_t) * group * (d_v + 1) + 3) / 4 * 4;
+}
 
 // Kernel launchers (defined in the .hip files). Return a hipError_t value.
 int launch_fwd(const FwdParams& p, int d_qk, int d_v, void* stream);

@@ -63,17 +63,18 @@ struct DeviceScope {
 void upload(MetaEntry& e, int device) {
   const Plan& p = *e.plan;
   DeviceScope scope(device);
-  const std::vector<int32_t>* parts[5] = {&p.kv_row, &p.tiles, &p.order, &p.kvtiles, &p.q_global};
-  size_t offs[5];
+  const std::vector<int32_t>* parts[7] = {&p.kv_row, &p.tiles, &p.order, &p.kvtiles,
+                                          &p.q_global, &p.items, &p.splits};
+  size_t offs[7];
   size_t bytes = 0;
-  for (int i = 0; i < 5; ++i) {
+  for (int i = 0; i < 7; ++i) {
     offs[i] = bytes;
     bytes += (parts[i]->size() * sizeof(int32_t) + 255) / 256 * 256;
   }
   void* base = nullptr;
   check_hip(hipMalloc(&base, bytes == 0 ? 256 : bytes), "hipMalloc(metadata)");
   std::vector<char> staging(bytes);
-  for (int i = 0; i < 5; ++i)
+  for (int i = 0; i < 7; ++i)
     if (!parts[i]->empty())
       std::memcpy(staging.data() + offs[i], parts[i]->data(), parts[i]->size() * sizeof(int32_t));
   const hipError_t err = hipMemcpy(base, staging.data(), bytes, hipMemcpyHostToDevice);
@@ -89,6 +90,8 @@ void upload(MetaEntry& e, int device) {
   e.dev.order = reinterpret_cast<const int32_t*>(b + offs[2]);
   e.dev.kvtiles = reinterpret_cast<const int32_t*>(b + offs[3]);
   e.dev.q_global = reinterpret_cast<const int32_t*>(b + offs[4]);
+  e.dev.items = reinterpret_cast<const int32_t*>(b + offs[5]);
+  e.dev.splits = reinterpret_cast<const int32_t*>(b + offs[6]);
 }
 
 // Least-recently-used cache of metadata entries. Entries still referenced by a
@@ -109,8 +112,8 @@ Cache& cache() {
 }
 
 std::string make_key(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank,
-                     int32_t block_t, int32_t block_n, int32_t device) {
-  const int32_t head[7] = {THD_META_VERSION, cp, rank, block_t, block_n, device, n_docs};
+                     int32_t block_t, int32_t block_n, int32_t concurrency, int32_t device) {
+  const int32_t head[8] = {THD_META_VERSION, cp, rank, block_t, block_n, concurrency, device, n_docs};
   std::string key(sizeof(head) + size_t(n_docs) * sizeof(int32_t), '\0');
   std::memcpy(&key[0], head, sizeof(head));
   std::memcpy(&key[sizeof(head)], seqlens, size_t(n_docs) * sizeof(int32_t));
@@ -199,18 +202,20 @@ int thd_plan_partition(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32
 }
 
 int thd_build_metadata(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank,
-                       int32_t block_t, int32_t block_n, int32_t device, thd_meta** out) {
+                       int32_t block_t, int32_t block_n, int32_t concurrency, int32_t device,
+                       thd_meta** out) {
   return guarded([&] {
     if (out == nullptr) fail(THD_EINVAL, "out is NULL");
     *out = nullptr;
     validate_partition(seqlens, n_docs, cp, rank);
     if (device < -1) fail(THD_EINVAL, "device must be >= -1");
+    if (concurrency < 0) fail(THD_EINVAL, "concurrency must be >= 0");
     if (device >= 0) {
       int count = 0;
       check_hip(hipGetDeviceCount(&count), "hipGetDeviceCount");
       if (device >= count) fail(THD_EINVAL, "no such device " + std::to_string(device));
     }
-    const std::string key = make_key(seqlens, n_docs, cp, rank, block_t, block_n, device);
+    const std::string key = make_key(seqlens, n_docs, cp, rank, block_t, block_n, concurrency, device);
     Cache& c = cache();
     std::lock_guard<std::mutex> lock(c.mu);
     auto hit = c.map.find(key);
@@ -223,7 +228,7 @@ int thd_build_metadata(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32
     } else {
       ++c.misses;
       auto e = std::make_shared<MetaEntry>();
-      e->plan = build_plan(seqlens, n_docs, cp, rank, block_t, block_n);
+      e->plan = build_plan(seqlens, n_docs, cp, rank, block_t, block_n, concurrency);
       if (device >= 0) {
         upload(*e, device);
         ++c.uploads;
@@ -254,6 +259,11 @@ int thd_meta_info(const thd_meta* meta, thd_meta_info_t* info) {
     info->n_kvtiles = int64_t(p.kvtiles.size() / 8);
     info->useful_pairs = p.useful_pairs;
     info->max_kv_tiles = p.max_kv_tiles;
+    info->n_items = int64_t(p.items.size() / 4);
+    info->n_splits = int64_t(p.splits.size() / 4);
+    info->n_part_slots = p.n_part_slots;
+    info->concurrency = p.concurrency;
+    info->kv_split = p.kv_split;
     info->n_docs = int32_t(p.seqlens.size());
     info->cp = p.cp;
     info->rank = p.rank;
@@ -276,6 +286,8 @@ int thd_meta_copy(const thd_meta* meta, int32_t field, int32_t* dst, int64_t cou
       case THD_FIELD_TILES: src = &p.tiles; break;
       case THD_FIELD_ORDER: src = &p.order; break;
       case THD_FIELD_KVTILES: src = &p.kvtiles; break;
+      case THD_FIELD_ITEMS: src = &p.items; break;
+      case THD_FIELD_SPLITS: src = &p.splits; break;
       default: fail(THD_EINVAL, "unknown field " + std::to_string(field));
     }
     if (count != int64_t(src->size()))
@@ -327,9 +339,22 @@ int thd_preferred_tiles(int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v, int3
   });
 }
 
+int thd_attn_fwd_workspace(const thd_meta* meta, int32_t hq, int32_t hkv, int32_t d_v,
+                           int64_t* bytes) {
+  return guarded([&] {
+    const Plan& p = *entry_of(meta).plan;
+    check_heads(hq, hkv);
+    if (d_v < 1) fail(THD_EINVAL, "d_v must be >= 1");
+    if (bytes == nullptr) fail(THD_EINVAL, "bytes is NULL");
+    *bytes = p.n_part_slots * hkv * fwd_partial_floats(p.block_t, hq / hkv, d_v) *
+             int64_t(sizeof(float));
+  });
+}
+
 int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void* v, void* o,
                  float* lse, int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
-                 float softmax_scale, void* hip_stream) {
+                 float softmax_scale, void* workspace, int64_t workspace_bytes,
+                 void* hip_stream) {
   return guarded([&] {
     const MetaEntry& e = entry_of(meta);
     const Plan& p = *e.plan;
@@ -345,9 +370,17 @@ int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void*
     check_ptr(v, "v", 16);
     check_ptr(o, "o", 16);
     check_ptr(lse, "lse", 16);
+    const int64_t need = p.n_part_slots * hkv * fwd_partial_floats(p.block_t, group, d_v) *
+                         int64_t(sizeof(float));
+    if (need > 0) {
+      check_ptr(workspace, "workspace", 16);
+      if (workspace_bytes < need)
+        fail(THD_EINVAL, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
+                             std::to_string(need));
+    }
     const DeviceMeta& d = device_meta(e);
-    const int64_t n_tiles = int64_t(p.tiles.size() / 8);
-    if (n_tiles * hkv >= (int64_t(1) << 31)) fail(THD_ERANGE, "grid too large");
+    const int64_t n_items = int64_t(p.items.size() / 4);
+    if (n_items * hkv >= (int64_t(1) << 31)) fail(THD_ERANGE, "grid too large");
     check_kv_bytes(p.total, hkv, d_qk, d_v);
     FwdParams fp{};
     fp.q = q;
@@ -355,10 +388,13 @@ int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void*
     fp.v = v;
     fp.o = o;
     fp.lse = lse;
+    fp.partial = static_cast<float*>(workspace);
     fp.tiles = d.tiles;
-    fp.order = d.order;
+    fp.items = d.items;
+    fp.splits = d.splits;
     fp.kv_row = d.kv_row;
-    fp.n_tiles = int32_t(n_tiles);
+    fp.n_items = int32_t(n_items);
+    fp.n_splits = int32_t(p.splits.size() / 4);
     fp.hq = hq;
     fp.hkv = hkv;
     fp.group = group;

@@ -6,12 +6,13 @@
 // rank-major K/V indexing in a single fused call; "Does this PR introduce any
 // user-facing change?": causal attention with the mask reset at every EOD).
 //
-// Work decomposition. One workgroup (4 waves, 256 lanes) handles one query
-// tile of one kv head: block_t tokens x G q heads = up to 128 rows, token-major
+// Work decomposition. One workgroup (4 waves, 256 lanes) handles one work
+// item (a query tile, or a part of its key range when the planner splits the
+// longest tiles for balance) of one kv head: block_t tokens x G q heads = up to 128 rows, token-major
 // (row = token * G + head-in-group), 32 rows per wave. All G heads of a kv head
 // share every K/V tile, so a K/V tile loaded once into LDS feeds 128 rows even
-// when tiles hold few tokens. Workgroup b takes kv head b % Hkv and tile
-// order[b / Hkv]: tiles are dispatched longest first, and since workgroups are
+// when tiles hold few tokens. Workgroup b takes kv head b % Hkv and work item
+// b / Hkv: items are dispatched longest first, and since workgroups are
 // spread round robin over the 8 XCDs, with Hkv = 8 each XCD (and its L2) serves
 // a single kv head.
 //
@@ -52,6 +53,7 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -130,14 +132,19 @@ __global__ __launch_bounds__(kFwdThreads, 2) void thd_fwd_kernel(FwdParams p) {
   const int half = lane >> 5;        // which 32-lane half
   const int lrow = lane & 31;
 
+  // Work item: KV tiles [kv_begin, kv_end) of one query tile (a whole tile
+  // unless its key range is split), for kv head blockIdx.x % Hkv.
   const int kvh = blockIdx.x % p.hkv;
-  const int tile = p.order[blockIdx.x / p.hkv];
+  const int32_t* item = p.items + size_t(blockIdx.x / p.hkv) * 4;
+  const int tile = item[0];
+  const int kv_begin = item[1];
+  const int kv_end = item[2];
+  const int part = item[3];
   const int32_t* td = p.tiles + size_t(tile) * 8;
   const int q_local0 = td[0];
   const int q_glob0 = td[1];
   const int n_rows = td[2];
   const int kv_start = td[5];
-  const int n_kv = td[6];
   const int n_full = td[7];
   const int key_last = q_glob0 + n_rows - 1;   // keys past this are seen by no row
 
@@ -239,18 +246,18 @@ __global__ __launch_bounds__(kFwdThreads, 2) void thd_fwd_kernel(FwdParams p) {
   }
   const float c2 = p.scale_log2;
 
-  // Prologue: rows of tiles 0 and 1, then tile 0's data.
-  fetch_rows(0, rows_cur);
+  // Prologue: rows of the first two KV tiles, then the first tile's data.
+  fetch_rows(kv_begin, rows_cur);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   issue_tile(smem0, rows_cur);
-  if (n_kv > 1) fetch_rows(1, rows_cur);
+  if (kv_begin + 1 < kv_end) fetch_rows(kv_begin + 1, rows_cur);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
 
   auto step = [&](int j, const char* stage, char* next) {
     // stage holds tile j; rows_cur holds tile j+1's rows.
-    if (j + 1 < n_kv) issue_tile(next, rows_cur);
-    if (j + 2 < n_kv) fetch_rows(j + 2, rows_nxt);
+    if (j + 1 < kv_end) issue_tile(next, rows_cur);
+    if (j + 2 < kv_end) fetch_rows(j + 2, rows_nxt);
 
     if (wave_active) {
       // S^T = K Q^T for keys [32*kb, 32*kb + 32) of the tile; each K fragment
@@ -346,9 +353,9 @@ __global__ __launch_bounds__(kFwdThreads, 2) void thd_fwd_kernel(FwdParams p) {
 #pragma unroll
     for (int i = 0; i < S::NROWS; ++i) rows_cur[i] = rows_nxt[i];
   };
-  for (int j = 0; j < n_kv; j += 2) {
+  for (int j = kv_begin; j < kv_end; j += 2) {
     step(j, smem0, smem1);
-    if (j + 1 < n_kv) step(j + 1, smem1, smem0);
+    if (j + 1 < kv_end) step(j + 1, smem1, smem0);
   }
 
 #pragma unroll
@@ -357,6 +364,25 @@ __global__ __launch_bounds__(kFwdThreads, 2) void thd_fwd_kernel(FwdParams p) {
     const float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 32);
     if (!valid[rb]) continue;
     const float inv = 1.0f / l_tot;
+    if (part >= 0) {
+      // Part of a split tile: its O normalised by its own sum, and its
+      // log2-sum-exp, for the combine kernel.
+      const int rows = p.block_t * G;
+      const int row = 32 * (RB * wave + rb) + lrow;
+      float* base = p.partial + (size_t(part) * p.hkv + kvh) * size_t(fwd_partial_floats(p.block_t, G, DV));
+      float* orow = base + size_t(row) * DV;
+#pragma unroll
+      for (int b = 0; b < S::DVB; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          f32x4 out;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[e] = acc[rb][b][4 * g + e] * inv;
+          *reinterpret_cast<f32x4*>(orow + 32 * b + 8 * g + 4 * half) = out;
+        }
+      if (half == 0) base[size_t(rows) * DV + row] = m_run[rb] + __builtin_amdgcn_logf(l_tot);
+      continue;
+    }
     __bf16* orow = static_cast<__bf16*>(p.o) + (size_t(q_local0 + tok[rb]) * p.hq + head[rb]) * DV;
 #pragma unroll
     for (int b = 0; b < S::DVB; ++b)
@@ -372,11 +398,64 @@ __global__ __launch_bounds__(kFwdThreads, 2) void thd_fwd_kernel(FwdParams p) {
   }
 }
 
+// Merges the parts of split tiles: O = sum_p w_p O_p / sum_p w_p with
+// w_p = 2^(lse_p - max lse), LSE = ln 2 * (max lse + log2 sum_p w_p). One
+// thread per (split tile, kv head, row, 4 columns): every load is independent,
+// so the pass is bandwidth-bound rather than latency-bound.
+template <int DV>
+__global__ __launch_bounds__(256) void thd_fwd_combine_kernel(FwdParams p) {
+  constexpr int CPR = DV / 4;                // 4-float column groups per row
+  const int G = p.group;
+  const int rows = p.block_t * G;
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t per_split = int64_t(p.hkv) * rows * CPR;
+  if (idx >= per_split * p.n_splits) return;
+  const int split = int(idx / per_split);
+  int rem = int(idx - split * per_split);
+  const int kvh = rem / (rows * CPR);
+  rem -= kvh * rows * CPR;
+  const int row = rem / CPR;
+  const int col = (rem - row * CPR) * 4;
+  const int32_t* sp = p.splits + size_t(split) * 4;
+  const int tile = sp[0], first = sp[1], n_parts = sp[2];
+  const int32_t* td = p.tiles + size_t(tile) * 8;
+  const int tok = row / G;
+  if (tok >= td[2]) return;                  // row past the tile's last token
+  const size_t slot_floats = size_t(fwd_partial_floats(p.block_t, G, DV));
+  const float* base0 = p.partial + (size_t(first) * p.hkv + kvh) * slot_floats;
+  const size_t part_stride = size_t(p.hkv) * slot_floats;
+  float mx = -INFINITY;
+  for (int q = 0; q < n_parts; ++q) mx = fmaxf(mx, base0[q * part_stride + size_t(rows) * DV + row]);
+  float wsum = 0.0f;
+  f32x4 acc = {};
+  for (int q = 0; q < n_parts; ++q) {
+    const float* base = base0 + q * part_stride;
+    const float w = __builtin_amdgcn_exp2f(base[size_t(rows) * DV + row] - mx);
+    wsum += w;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(base + size_t(row) * DV + col);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, v[e], acc[e]);
+  }
+  const float inv = 1.0f / wsum;
+  const int head = kvh * G + (row - tok * G);
+  const size_t orow = size_t(td[0] + tok) * p.hq + head;
+  bf16x4 out;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[e] = static_cast<__bf16>(acc[e] * inv);
+  *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.o) + orow * DV + col) = out;
+  if (col == 0) p.lse[orow] = (mx + __builtin_amdgcn_logf(wsum)) * kLn2;
+}
+
 template <int DQK, int DV>
 int launch(const FwdParams& p, void* stream) {
-  const dim3 grid(unsigned(int64_t(p.n_tiles) * p.hkv));
-  hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV>), grid, dim3(kFwdThreads), 0,
-                     static_cast<hipStream_t>(stream), p);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const dim3 grid(unsigned(int64_t(p.n_items) * p.hkv));
+  hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV>), grid, dim3(kFwdThreads), 0, st, p);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess || p.n_splits == 0) return int(err);
+  const int64_t threads = int64_t(p.n_splits) * p.hkv * p.block_t * p.group * (DV / 4);
+  hipLaunchKernelGGL((thd_fwd_combine_kernel<DV>), dim3(unsigned((threads + 255) / 256)),
+                     dim3(256), 0, st, p);
   return int(hipGetLastError());
 }
 

@@ -14,7 +14,8 @@
 // chunk, so every row of a tile belongs to the same document and its KV loop
 // starts at the document's first key; the loop stops at the last row's own
 // position, and only the tiles past the first row's position need the causal
-// compare. The arrays are built in one pass with closed forms.
+// compare. The arrays are built in one pass with closed forms. The longest
+// tiles' key ranges may be split into several forward work items (below).
 #include <algorithm>
 #include <cstring>
 #include <numeric>
@@ -70,10 +71,12 @@ void plan_partition(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t 
 }
 
 std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t cp,
-                                 int32_t rank, int32_t block_t, int32_t block_n) {
+                                 int32_t rank, int32_t block_t, int32_t block_n,
+                                 int32_t concurrency) {
   const int64_t total = validate_partition(seqlens, n_docs, cp, rank);
   if (block_t < 1 || block_n < 1 || block_t > 4096 || block_n > 4096)
     fail(THD_ERANGE, "tile sizes must be in [1, 4096]");
+  if (concurrency < 0) fail(THD_EINVAL, "concurrency must be >= 0");
   auto plan = std::make_unique<Plan>();
   Plan& p = *plan;
   p.seqlens.assign(seqlens, seqlens + n_docs);
@@ -81,6 +84,7 @@ std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t
   p.rank = rank;
   p.block_t = block_t;
   p.block_n = block_n;
+  p.concurrency = concurrency;
   p.total = total;
   p.local = total / cp;
   p.q_global.resize(p.local);
@@ -144,6 +148,48 @@ std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t
     }
     cu += seqlens[i];
   }
+  // Forward work items: the key range of the longest tiles is cut into parts
+  // when the tiles alone are too few to keep the device busy, so no single
+  // workgroup's loop is much longer than the average per workgroup slot. Every
+  // part starts with a KV tile all its rows see whole (cuts at or before
+  // n_full - 1), so no row of a part is empty.
+  int64_t total_kv = 0;
+  for (int64_t t = 0; t < n_tiles; ++t) total_kv += p.tiles[size_t(t) * 8 + 6];
+  if (concurrency > 0 && n_tiles < 2 * int64_t(concurrency))
+    p.kv_split = int32_t(std::max<int64_t>((total_kv + concurrency - 1) / concurrency, 8));
+  std::vector<int32_t> natural;
+  for (int64_t t = 0; t < n_tiles; ++t) {
+    const int64_t n_kv = p.tiles[size_t(t) * 8 + 6];
+    const int64_t n_full = p.tiles[size_t(t) * 8 + 7];
+    if (p.kv_split == 0 || n_kv <= p.kv_split || n_full < 2) {
+      const int32_t rec[4] = {int32_t(t), 0, int32_t(n_kv), -1};
+      natural.insert(natural.end(), rec, rec + 4);
+      continue;
+    }
+    const int64_t count = std::min<int64_t>((n_kv + p.kv_split - 1) / p.kv_split, n_full);
+    std::vector<int64_t> bounds(count + 1);
+    bounds[0] = 0;
+    bounds[count] = n_kv;
+    for (int64_t i = 1; i < count; ++i) bounds[i] = i * n_kv / count;
+    bounds[count - 1] = std::min(bounds[count - 1], n_full - 1);
+    for (int64_t i = count - 2; i >= 1; --i) bounds[i] = std::min(bounds[i], bounds[i + 1] - 1);
+    const int32_t srec[4] = {int32_t(t), int32_t(p.n_part_slots), int32_t(count), 0};
+    p.splits.insert(p.splits.end(), srec, srec + 4);
+    for (int64_t i = 0; i < count; ++i) {
+      const int32_t rec[4] = {int32_t(t), int32_t(bounds[i]), int32_t(bounds[i + 1]),
+                              int32_t(p.n_part_slots++)};
+      natural.insert(natural.end(), rec, rec + 4);
+    }
+  }
+  const int64_t n_items = int64_t(natural.size() / 4);
+  std::vector<int32_t> rank_of(n_items);
+  std::iota(rank_of.begin(), rank_of.end(), 0);
+  std::stable_sort(rank_of.begin(), rank_of.end(), [&](int32_t a, int32_t b) {
+    return natural[size_t(a) * 4 + 2] - natural[size_t(a) * 4 + 1] >
+           natural[size_t(b) * 4 + 2] - natural[size_t(b) * 4 + 1];
+  });
+  p.items.reserve(natural.size());
+  for (int32_t i : rank_of) p.items.insert(p.items.end(), &natural[size_t(i) * 4], &natural[size_t(i) * 4] + 4);
   return plan;
 }
 

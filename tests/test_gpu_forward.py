@@ -59,6 +59,41 @@ def test_forward_matches_oracle_small(case):
     assert_close(lse.cpu().double().numpy(), want_lse, "LSE", max_abs=LSE_ABS, mean_abs=LSE_ABS)
 
 
+SPLIT = [
+    # (seed, lengths, cp, rank, hq, hkv, dqk, dv): long documents, so the
+    # key ranges of the late chunk's tiles are cut into several parts
+    (71, [2048, 512, 1024], 2, 1, 16, 4, 128, 128),
+    (72, [4096, 96], 4, 0, 8, 8, 64, 64),
+    (73, [3072, 1040], 8, 3, 16, 16, 192, 128),
+    (74, [1512, 300], 3, 1, 12, 4, 128, 128),      # group 3: 126-row tiles
+]
+
+
+@pytest.mark.parametrize("case", SPLIT, ids=lambda c: f"seed{c[0]}")
+@pytest.mark.parametrize("concurrency", [64, 100000])
+def test_forward_split_key_ranges_match_oracle(case, concurrency):
+    seed, lengths, cp, rank, hq, hkv, dqk, dv = case
+    b = workloads.small_case(seed, lengths, cp, hq, hkv, dqk, dv, rank=rank)
+    dev = device()
+    q, k, v = b.q.to(dev), b.k.to(dev), b.v.to(dev)
+    meta = thd.device_metadata(seqlens=b.lengths, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=dqk,
+                               d_v=dv, device=0, concurrency=concurrency)
+    info = meta.info()
+    print(f"[fwd split] seed={seed} concurrency={concurrency} kv_split={info['kv_split']} "
+          f"splits={info['n_splits']} parts={info['n_part_slots']}", flush=True)
+    assert info["n_splits"] > 0
+    o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=b.lengths, cp=cp, rank=rank, meta=meta)
+    torch.cuda.synchronize()
+    want_o, want_lse = oatt.attn_fwd64(to64(b.q), to64(b.k), to64(b.v), lengths, cp, rank)
+    assert_close(to64(o), want_o, "O")
+    assert_close(lse.cpu().double().numpy(), want_lse, "LSE", max_abs=LSE_ABS, mean_abs=LSE_ABS)
+    # the same rows without splitting agree closely (different summation order only)
+    o1, lse1 = thd.attn_fwd(q=q, k=k, v=v, seqlens=b.lengths, cp=cp, rank=rank, concurrency=0)
+    torch.cuda.synchronize()
+    assert (o.float() - o1.float()).abs().max().item() <= 1e-2
+    assert (lse - lse1).abs().max().item() <= 1e-4
+
+
 def test_forward_custom_scale():
     b = workloads.small_case(21, [64, 192], 2, 8, 2, 128, 128, rank=1)
     o, lse = _run(b, scale=0.3)

@@ -34,8 +34,9 @@ def test_library_exports_every_declared_symbol():
     assert sorted(thd.EXPORTS) == declared
 
 
-def _compare_plan(lengths, cp, rank, bt, bn):
-    m = thd.build_metadata(seqlens=lengths, cp=cp, rank=rank, block_t=bt, block_n=bn)
+def _compare_plan(lengths, cp, rank, bt, bn, concurrency=0):
+    m = thd.build_metadata(seqlens=lengths, cp=cp, rank=rank, block_t=bt, block_n=bn,
+                           concurrency=concurrency)
     assert np.array_equal(m.field("q_global"), opart.q_global(lengths, cp, rank))
     assert np.array_equal(m.field("kv_row"), opart.kv_row(lengths, cp))
     assert np.array_equal(m.field("chunk_off"), opart.chunk_off(lengths, cp))
@@ -43,7 +44,12 @@ def _compare_plan(lengths, cp, rank, bt, bn):
     assert np.array_equal(m.field("tiles"), tt)
     assert np.array_equal(m.field("order"), ometa.order(tt))
     assert np.array_equal(m.field("kvtiles"), ometa.kvtiles(lengths, cp, rank, bt, bn))
+    items, splits = ometa.items_and_splits(tt, concurrency)
+    assert np.array_equal(m.field("items"), items)
+    assert np.array_equal(m.field("splits"), splits)
     info = m.info()
+    assert info["kv_split"] == ometa.kv_split_for(tt, concurrency)
+    assert info["n_part_slots"] == int(splits[:, 2].sum()) if splits.size else info["n_part_slots"] == 0
     assert info["useful_pairs"] == ometa.useful_pairs_closed_form(lengths, cp)
     assert info["max_kv_tiles"] == int(tt[:, 6].max())
     assert info["version"] == ometa.VERSION == thd.META_VERSION
@@ -59,7 +65,8 @@ def test_metadata_bit_exact_on_workloads(w):
     bt, bn = thd.preferred_tiles(hq=w.hq, hkv=w.hkv, d_qk=w.d_qk, d_v=w.d_v)
     ranks = sorted({w.rank, 0, w.cp - 1})
     for rank in ranks:
-        _compare_plan(lengths, w.cp, rank, bt, bn)
+        for concurrency in (0, 512 // w.hkv, 7):
+            _compare_plan(lengths, w.cp, rank, bt, bn, concurrency)
 
 
 @pytest.mark.parametrize("seed", range(12))
@@ -69,7 +76,7 @@ def test_metadata_bit_exact_random(seed):
     lengths = workloads.random_lengths(rng, int(rng.integers(1, 9)), cp, 40)
     bt = int(rng.choice([1, 3, 16, 32, 128]))
     bn = int(rng.choice([1, 5, 64]))
-    _compare_plan(lengths, cp, int(rng.integers(0, cp)), bt, bn)
+    _compare_plan(lengths, cp, int(rng.integers(0, cp)), bt, bn, int(rng.choice([0, 1, 4, 50])))
 
 
 def test_preferred_tiles():
@@ -121,11 +128,12 @@ def test_metadata_argument_errors():
 def test_null_pointers_return_errors():
     lib = thd._lib
     assert lib.thd_plan_partition(None, 1, 1, 0, None, None, None, None, None) == -1
-    assert lib.thd_build_metadata(None, 1, 1, 0, 1, 1, -1, None) == -1
+    assert lib.thd_build_metadata(None, 1, 1, 0, 1, 1, 0, -1, None) == -1
     assert lib.thd_meta_info(None, None) == -1
     assert lib.thd_meta_copy(None, 0, None, 0) == -1
     lib.thd_meta_release(None)
-    assert lib.thd_attn_fwd(None, None, None, None, None, None, 1, 1, 128, 128, 1.0, None) == -1
+    assert lib.thd_attn_fwd(None, None, None, None, None, None, 1, 1, 128, 128, 1.0, None, 0,
+                            None) == -1
     assert b"NULL" in lib.thd_last_error()
     m = thd.build_metadata(seqlens=[8], cp=1, rank=0, block_t=4, block_n=64)
     n = ctypes.c_int32()
@@ -140,18 +148,24 @@ def test_forward_rejects_host_only_metadata_and_bad_arguments():
     ptr = (ctypes.addressof(buf) + 15) // 16 * 16
     lib = thd._lib
     args = [m.handle, ptr, ptr, ptr, ptr, ptr]
+    tail = [None, 0, None]
     # unsupported head dims are refused before any device check
-    assert lib.thd_attn_fwd(*args, 32, 8, 96, 96, 0.1, None) == -8
+    assert lib.thd_attn_fwd(*args, 32, 8, 96, 96, 0.1, *tail) == -8
     # bad scale
-    assert lib.thd_attn_fwd(*args, 32, 8, 128, 128, 0.0, None) == -1
-    assert lib.thd_attn_fwd(*args, 32, 8, 128, 128, float("nan"), None) == -1
+    assert lib.thd_attn_fwd(*args, 32, 8, 128, 128, 0.0, *tail) == -1
+    assert lib.thd_attn_fwd(*args, 32, 8, 128, 128, float("nan"), *tail) == -1
     # tile sizes that do not fit the group size
-    assert lib.thd_attn_fwd(*args, 64, 8, 128, 128, 0.1, None) == -5
+    assert lib.thd_attn_fwd(*args, 64, 8, 128, 128, 0.1, *tail) == -5
     # misaligned pointer
-    assert lib.thd_attn_fwd(m.handle, ptr + 2, ptr, ptr, ptr, ptr, 32, 8, 128, 128, 0.1, None) == -4
+    assert lib.thd_attn_fwd(m.handle, ptr + 2, ptr, ptr, ptr, ptr, 32, 8, 128, 128, 0.1, *tail) == -4
     # host-only metadata cannot launch
-    assert lib.thd_attn_fwd(*args, 32, 8, 128, 128, 0.1, None) == -5
+    assert lib.thd_attn_fwd(*args, 32, 8, 128, 128, 0.1, *tail) == -5
     assert b"device" in lib.thd_last_error()
+    # a split plan needs its workspace
+    ms = thd.build_metadata(seqlens=[4096], cp=1, rank=0, block_t=32, block_n=64, concurrency=256)
+    assert ms.info()["n_part_slots"] > 0
+    assert lib.thd_attn_fwd(ms.handle, ptr, ptr, ptr, ptr, ptr, 32, 8, 128, 128, 0.1, *tail) == -1
+    assert b"workspace" in lib.thd_last_error()
 
 
 def test_cache_hits_and_key_completeness():
@@ -163,12 +177,12 @@ def test_cache_hits_and_key_completeness():
     c = thd.build_metadata(seqlens=[16, 8, 8], cp=2, rank=0, block_t=4, block_n=8)
     assert c.info()["cache_hit"] == 0
     assert not np.array_equal(a.field("q_global"), c.field("q_global"))
-    for kw in (dict(rank=1), dict(block_t=2), dict(block_n=4)):
+    for kw in (dict(rank=1), dict(block_t=2), dict(block_n=4), dict(concurrency=3)):
         args = dict(seqlens=[8, 16, 8], cp=2, rank=0, block_t=4, block_n=8)
         args.update(kw)
         assert thd.build_metadata(**args).info()["cache_hit"] == 0
     st = thd.cache_stats()
-    assert st["hits"] == 1 and st["misses"] == 5 and st["uploads"] == 0
+    assert st["hits"] == 1 and st["misses"] == 6 and st["uploads"] == 0
     # a handle outlives the cache entry it came from
     thd.cache_clear()
     assert np.array_equal(a.field("tiles"), ometa.tiles([8, 16, 8], 2, 0, 4, 8))

@@ -155,3 +155,41 @@ def test_workload_lengths_are_valid(w):
     lengths = workloads.draw_lengths(w, np.random.default_rng(w.index))
     assert int(lengths.sum()) == w.total
     assert all(int(x) % (2 * w.cp) == 0 and int(x) > 0 for x in lengths)
+
+
+def test_work_items_match_hand_derivation():
+    g = read_records("items_small.txt")
+    tt = metadata.tiles([64], 1, 0, 8, 4)
+    items, splits = metadata.items_and_splits(tt, 8)
+    assert items.tolist() == g["itemA"] and splits.tolist() == g["splitA"]
+    tt = metadata.tiles([256], 1, 0, 128, 4)
+    items, splits = metadata.items_and_splits(tt, 12)
+    assert items.tolist() == g["itemB"] and splits.tolist() == g["splitB"]
+
+
+@pytest.mark.parametrize("concurrency", [0, 1, 3, 16, 64, 1000])
+def test_work_items_cover_each_tile_once(concurrency):
+    rng = np.random.default_rng(concurrency)
+    for cp in (1, 2, 4):
+        lengths = workloads.random_lengths(rng, 5, cp, 60)
+        for rank in range(cp):
+            tt = metadata.tiles(lengths, cp, rank, 8, 4)
+            items, splits = metadata.items_and_splits(tt, concurrency)
+            lens = items[:, 2] - items[:, 1]
+            assert all(lens[:-1] >= lens[1:])
+            split_tiles = {int(r[0]): r for r in splits.tolist()}
+            slots = []
+            for t in range(tt.shape[0]):
+                mine = sorted((int(b), int(e), int(s)) for tile, b, e, s in items.tolist() if tile == t)
+                # the parts tile [0, n_kv) exactly, in order
+                assert mine[0][0] == 0 and mine[-1][1] == tt[t, 6]
+                assert all(mine[i][1] == mine[i + 1][0] for i in range(len(mine) - 1))
+                if len(mine) == 1:
+                    assert mine[0][2] == -1 and t not in split_tiles
+                    continue
+                first, count = split_tiles[t][1], split_tiles[t][2]
+                assert [m[2] for m in mine] == list(range(first, first + count))
+                slots.extend(m[2] for m in mine)
+                # every part starts with a KV tile all rows see whole
+                assert all(m[0] <= tt[t, 7] - 1 for m in mine)
+            assert sorted(slots) == list(range(len(slots)))
