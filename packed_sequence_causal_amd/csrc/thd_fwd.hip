@@ -294,17 +294,26 @@ __global__ __launch_bounds__(kFwdThreads, 2) void thd_fwd_kernel(FwdParams p) {
             }
         }
 
-        float mx = s[rb][0][0];
+        // This lane's half of the row maximum, as a tree (short chains).
+        constexpr int NV = 16 * S::KB;
+        float mv[NV];
 #pragma unroll
         for (int kb2 = 0; kb2 < S::KB; ++kb2)
 #pragma unroll
-          for (int r = (kb2 == 0 ? 1 : 0); r < 16; ++r) mx = fmaxf(mx, s[rb][kb2][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // Each row decides on its own (so a row's arithmetic never depends on
-        // its neighbours); the wave only skips the rescale when no row needs it.
-        const float m_tile = mx * c2;
-        const bool need = m_tile > m_run[rb] + kRescaleSlack;
-        if (__any(need)) {
+          for (int r = 0; r < 16; ++r) mv[16 * kb2 + r] = s[rb][kb2][r];
+#pragma unroll
+        for (int w = NV / 2; w >= 1; w /= 2)
+#pragma unroll
+          for (int i = 0; i < w; ++i) mv[i] = fmaxf(mv[i], mv[i + w]);
+        const float m_half = mv[0] * c2;
+        // A row is rescaled only when its maximum grows by more than the slack,
+        // which a row can only do if one of its halves does: only then do the
+        // halves exchange maxima. Each row decides on its own (its arithmetic
+        // never depends on its neighbours); the wave skips the whole step when
+        // no row needs it, which is the common case.
+        if (__any(m_half > m_run[rb] + kRescaleSlack)) {
+          const float m_tile = fmaxf(m_half, __shfl_xor(m_half, 32));
+          const bool need = m_tile > m_run[rb] + kRescaleSlack;
           const float alpha = need ? __builtin_amdgcn_exp2f(m_run[rb] - m_tile) : 1.0f;
 #pragma unroll
           for (int b = 0; b < S::DVB; ++b)
@@ -315,14 +324,16 @@ __global__ __launch_bounds__(kFwdThreads, 2) void thd_fwd_kernel(FwdParams p) {
         }
 
         const float neg_m = -m_run[rb];
+        float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // independent partial sums
 #pragma unroll
         for (int kb2 = 0; kb2 < S::KB; ++kb2)
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][kb2][r], c2, neg_m));
-            l_run[rb] += e;
+            ls[r & 3] += e;
             pb[rb][2 * kb2 + (r >> 3)][r & 7] = static_cast<__bf16>(e);
           }
+        l_run[rb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
       }
 
       // O^T += V^T P^T, 16 keys per MFMA: keys 16t + 4*half + {0..3, 8..11};
