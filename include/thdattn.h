@@ -189,7 +189,8 @@ int thd_attn_bwd_workspace(const thd_meta* meta, int32_t hq, int64_t* bytes);
  * in full (zeros for keys no local query sees). The softmax-gradient term
  * D = rowsum(dO * O) is recomputed as rowsum(P * dP) from the scores, which is
  * equal for the exact O, so the forward's rounded o is not an input. The
- * workspace (size from thd_attn_bwd_workspace) holds D. */
+ * workspace (size from thd_attn_bwd_workspace, 16-byte aligned) holds D and
+ * the log-sum-exp in base 2 for every local row and q head. */
 int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void* v,
                  const float* lse, const void* d_o,
                  float* dq, float* dk, float* dv,

@@ -116,7 +116,8 @@ struct BwdParams {
   float* dq;
   float* dk;
   float* dv;
-  float* delta;       // workspace [T_local, Hq]
+  float* delta;       // workspace: D [T_local, Hq]
+  float* lse2;        // workspace: lse * log2(e) [T_local, Hq]
   const int32_t* tiles;
   const int32_t* kvtiles;
   const int32_t* kv_row;
@@ -125,6 +126,12 @@ struct BwdParams {
   float scale;        // softmax_scale
   float scale_log2;   // softmax_scale * log2(e)
 };
+
+// Bytes of one [T_local, Hq] fp32 array in the backward workspace, padded so
+// the next array starts 256-byte aligned; the workspace holds two (D, lse2).
+inline int64_t bwd_ws_array_bytes(int64_t local, int32_t hq) {
+  return (local * hq * int64_t(sizeof(float)) + 255) / 256 * 256;
+}
 
 int launch_bwd(const BwdParams& p, int d_qk, int d_v, void* stream);
 bool bwd_supported(int d_qk, int d_v);

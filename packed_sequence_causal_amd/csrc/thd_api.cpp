@@ -410,7 +410,7 @@ int thd_attn_bwd_workspace(const thd_meta* meta, int32_t hq, int64_t* bytes) {
     const Plan& p = *entry_of(meta).plan;
     if (hq < 1) fail(THD_EINVAL, "hq must be >= 1");
     if (bytes == nullptr) fail(THD_EINVAL, "bytes is NULL");
-    *bytes = (p.local * hq * int64_t(sizeof(float)) + 255) / 256 * 256;
+    *bytes = 2 * bwd_ws_array_bytes(p.local, hq);
   });
 }
 
@@ -437,7 +437,7 @@ int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void*
     check_ptr(dk, "dk", 16);
     check_ptr(dv, "dv", 16);
     check_ptr(workspace, "workspace", 16);
-    const int64_t need = (p.local * hq * int64_t(sizeof(float)) + 255) / 256 * 256;
+    const int64_t need = 2 * bwd_ws_array_bytes(p.local, hq);
     if (workspace_bytes < need)
       fail(THD_EINVAL, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
                            std::to_string(need));
@@ -457,6 +457,7 @@ int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void*
     bp.dk = dk;
     bp.dv = dv;
     bp.delta = static_cast<float*>(workspace);
+    bp.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_ws_array_bytes(p.local, hq));
     bp.tiles = d.tiles;
     bp.kvtiles = d.kvtiles;
     bp.kv_row = d.kv_row;

@@ -49,8 +49,12 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(4))) const int32_t cint32_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaitVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0)
@@ -77,6 +81,25 @@ __device__ __forceinline__ bf16x8 tr_pair(const char* base, int off0, int off1) 
   const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off0));
   const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(base + off1));
   return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
+// Returns x unchanged, hidden from the optimiser: a mask applied to the result
+// in the same basic block survives, so instruction selection can see that a
+// product fits a 24-bit multiply (full rate, where a 32-bit one is quarter rate).
+__device__ __forceinline__ uint32_t opaque(uint32_t x) {
+  asm volatile("" : "+s"(x));
+  return x;
+}
+
+// Splits (x0, x1) into two packed bf16 pairs: hi holds x truncated to bf16
+// (the upper half of each float, one byte permute), lo holds x - hi (exact in
+// fp32) rounded to bf16. hi + lo equals x to within 2^-16 of |x|.
+__device__ __forceinline__ void split_pair(float x0, float x1, unsigned& hi, unsigned& lo) {
+  const unsigned u0 = __builtin_bit_cast(unsigned, x0), u1 = __builtin_bit_cast(unsigned, x1);
+  hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+  const float r0 = x0 - __builtin_bit_cast(float, u0 & 0xffff0000u);
+  const float r1 = x1 - __builtin_bit_cast(float, u1 & 0xffff0000u);
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
 }
 
 // Byte offset of the 8-byte piece (row, col .. col+3) in a row-major tile with
@@ -256,7 +279,10 @@ __global__ __launch_bounds__(kWaves * 64, DQK > 128 ? 1 : 2) void thd_bwd_dq_ker
   if constexpr (DELTA) {
     if (!wave_active) return;
     const float total = dsum + __shfl_xor(dsum, 32);
-    if (valid && half == 0) p.delta[qrow_idx] = total;
+    if (valid && half == 0) {
+      p.delta[qrow_idx] = total;
+      p.lse2[qrow_idx] = lse2;
+    }
     return;
   }
   if (!valid) return;
@@ -273,222 +299,371 @@ __global__ __launch_bounds__(kWaves * 64, DQK > 128 ? 1 : 2) void thd_bwd_dq_ker
 }
 
 // ---------------------------------------------------------------- dK, dV
-constexpr int kDkvWaves = 2;
+// One workgroup of 4 waves per (64-key tile, kv head); wave w owns keys
+// 16w .. 16w+15 of the tile, so that its K and V operands and its dK, dV
+// accumulators fit two waves per SIMD (whose vector and matrix work then
+// overlap). Row blocks of 32 rows stream through a three-stage LDS ring.
+constexpr int kDkvWaves = 4;
+constexpr int kDkvKeysPerWave = 16;
 constexpr int kRowsPerBlock = 32;
+
+// 4-byte global -> LDS copy: lane i's 4 bytes land at lds + 4 * i.
+__device__ __forceinline__ void load_lds4(const char* src, char* lds) {
+  __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 4, 0, 0);
+}
+
+// Workgroup barrier for LDS only. __syncthreads() also waits for every vector
+// memory operation in flight (its release fence covers the copies into LDS),
+// which would drain the ring; the copies a stage needs are waited for
+// explicitly with wait_vmcnt before this barrier.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// s_waitcnt vmcnt(N), leaving the other counters alone.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt(0x0F70 | (N & 15) | ((N >> 4) << 14));
+}
+
+// Chunk swizzle of the dK/dV kernel's row blocks. For 16 chunks per row it was
+// chosen by timing both read patterns of this kernel on gfx950: 16 consecutive
+// rows at one chunk per 16-lane group (operands of S and dP; two other XOR
+// swizzles run these reads about 1.7 times slower) and the transposed reads of
+// the dV and dK operands.
+template <int CPR>
+__device__ __forceinline__ int swz_kv(int r) {
+  if constexpr (CPR == 16) {
+    return ((r & 1) << 3) | ((r >> 1) & 7);
+  } else {
+    return (r >> 1) & 7;
+  }
+}
+
+// Byte offset of the 8-byte piece (row, col .. col+3) in a row-major tile with
+// ROWB-byte rows whose 16-byte chunks are swizzled by swz_kv<CPR>(row).
+template <int CPR, int ROWB>
+__device__ __forceinline__ int piece_kv(int row, int col) {
+  return row * ROWB + (((col >> 3) ^ swz_kv<CPR>(row)) << 4) + ((col & 4) << 1);
+}
 
 template <int DQK, int DV>
 struct DkvShape {
   static constexpr int KCPR = DQK / 8, VCPR = DV / 8;
   static constexpr int KROWB = DQK * 2, VROWB = DV * 2;
-  static constexpr int KBYTES = BN * KROWB, VBYTES = BN * VROWB;
   static constexpr int QBYTES = kRowsPerBlock * KROWB, OBYTES = kRowsPerBlock * VROWB;
-  // stage: Q block, dO block, then per-row lse (log2 units), D, and query position
-  static constexpr int STAGE = QBYTES + OBYTES + 3 * kRowsPerBlock * 4;
-  static constexpr int KV_BYTES = KBYTES + VBYTES;
-  static constexpr int K_IPW = BN * KCPR / 64 / kDkvWaves;     // K tile loads per wave
-  static constexpr int V_IPW = BN * VCPR / 64 / kDkvWaves;
-  static constexpr int Q_IPW = kRowsPerBlock * KCPR / 64 / kDkvWaves;
+  // stage: Q block, dO block, then per-row lse2 and D
+  static constexpr int INFO = QBYTES + OBYTES;
+  static constexpr int STAGE = INFO + 2 * kRowsPerBlock * 4;
+  static constexpr int Q_IPW = kRowsPerBlock * KCPR / 64 / kDkvWaves;   // copies per wave
   static constexpr int O_IPW = kRowsPerBlock * VCPR / 64 / kDkvWaves;
-  static constexpr int KSTEPS = DQK / 16, VSTEPS = DV / 16, DQB = DQK / 32, DVB = DV / 32;
+  static constexpr int LOADS = Q_IPW + O_IPW;   // waves 0 and 1 issue one row-info copy more
+  static constexpr int KS = DQK / 32, VS = DV / 32;           // k-steps of S and dP
+  static constexpr int KT = DQK / 16, VT = DV / 16;           // 16-wide tiles of dK and dV
   static_assert(kRowsPerBlock * KCPR % (64 * kDkvWaves) == 0, "Q block must split evenly");
   static_assert(kRowsPerBlock * VCPR % (64 * kDkvWaves) == 0, "dO block must split evenly");
 };
 
+// A block of 32 consecutive rows (token-major: all G heads of a kv head) of
+// one query tile; t >= q_end marks the end of the walk.
+struct RowBlock {
+  int t, sb;    // query tile, block within it
+  int qg;       // tile's first global position
+  int nrg;      // tile's rows: tokens times G
+  size_t base;  // index into [T_local * Hq] of the tile's first row
+};
+
 template <int DQK, int DV>
-__global__ __launch_bounds__(kDkvWaves * 64, 1) void thd_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kDkvWaves * 64, 2) void thd_bwd_dkdv_kernel(BwdParams p) {
   using S = DkvShape<DQK, DV>;
-  __shared__ __attribute__((aligned(1024))) char smem[S::KV_BYTES + 2 * S::STAGE];
-  char* const kv_lds = smem;
-  char* const ring = smem + S::KV_BYTES;
+  // Separate arrays, so the compiler can tell that reading one stage needs
+  // no wait on copies still landing in another.
+  __shared__ __attribute__((aligned(1024))) char stage0[S::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage1[S::STAGE];
+  __shared__ __attribute__((aligned(1024))) char stage2[S::STAGE];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int half = lane >> 5;
-  const int lrow = lane & 31;
+  const int grp = lane >> 4;   // 16-lane group
+  const int lr = lane & 15;
 
   const int kvh = blockIdx.x % p.hkv;
   const int kt = blockIdx.x / p.hkv;
-  const int32_t* kd = p.kvtiles + size_t(kt) * 8;
+  // The tables are read-only for the whole launch: reading them through the
+  // constant address space lets uniform reads use scalar loads.
+  const cint32_t* kd = (const cint32_t*)(p.kvtiles) + size_t(kt) * 8;
   const int ks = kd[1], nk = kd[2], qb = kd[3], qe = kd[4];
   const int G = p.group;
   const int hkv = p.hkv;
   const int hq = p.hq;
-  const char* __restrict__ kb = static_cast<const char*>(p.k);
-  const char* __restrict__ vb = static_cast<const char*>(p.v);
+  // floor(x / G) = (x * ginv) >> 16 for 0 <= x < 65536 / G; rows within a
+  // tile number at most 128 and G at most 128.
+  const uint32_t ginv = 65536u / uint32_t(G) + 1u;
+  const uint32_t hq_minus_g = uint32_t(hq - G);
   const char* __restrict__ qbase = static_cast<const char*>(p.q);
   const char* __restrict__ obase = static_cast<const char*>(p.d_o);
 
-  // K and V of this key tile (keys past the tile's end are clamped to its last
-  // key; they are masked out below and never stored).
-  {
+  // This lane's key (lane % 16 of the wave's 16) as the B operand of S = Q K^T
+  // and dP = dO V^T, held in registers for the whole walk. Keys past the
+  // tile's end repeat its last key; their accumulators are never stored.
+  const int key_rel = wave * kDkvKeysPerWave + lr;
+  const int key = ks + key_rel;
+  bf16x8 kf[S::KS], vf[S::VS];
+  if (qb < qe) {
+    const size_t kvr = size_t(p.kv_row[ks + min(key_rel, nk - 1)]) * hkv + kvh;
+    const __bf16* krow = static_cast<const __bf16*>(p.k) + kvr * DQK + 8 * grp;
+    const __bf16* vrow = static_cast<const __bf16*>(p.v) + kvr * DV + 8 * grp;
 #pragma unroll
-    for (int i = 0; i < S::K_IPW; ++i) {
-      const int q = (wave * S::K_IPW + i) * 64 + lane;
-      const int r = q / S::KCPR;
-      const int c = (q - r * S::KCPR) ^ swz<S::KCPR>(r);
-      const int grow = p.kv_row[ks + min(r, nk - 1)];
-      const char* src = kb + (size_t(grow) * hkv + kvh) * S::KROWB + c * 16;
-      load_lds16(src, kv_lds + (wave * S::K_IPW + i) * 1024);
-    }
+    for (int st = 0; st < S::KS; ++st) kf[st] = *reinterpret_cast<const bf16x8*>(krow + 32 * st);
 #pragma unroll
-    for (int i = 0; i < S::V_IPW; ++i) {
-      const int q = (wave * S::V_IPW + i) * 64 + lane;
-      const int r = q / S::VCPR;
-      const int c = (q - r * S::VCPR) ^ swz<S::VCPR>(r);
-      const int grow = p.kv_row[ks + min(r, nk - 1)];
-      const char* src = vb + (size_t(grow) * hkv + kvh) * S::VROWB + c * 16;
-      load_lds16(src, kv_lds + S::KBYTES + (wave * S::V_IPW + i) * 1024);
-    }
+    for (int st = 0; st < S::VS; ++st) vf[st] = *reinterpret_cast<const bf16x8*>(vrow + 32 * st);
+  } else {
+#pragma unroll
+    for (int st = 0; st < S::KS; ++st) kf[st] = bf16x8{};
+#pragma unroll
+    for (int st = 0; st < S::VS; ++st) vf[st] = bf16x8{};
   }
 
-  // Row blocks: query tile t in [qb, qe), block sb of its n_rows * G rows.
-  struct Block {
-    int t, sb;
+  // Records (first local row, first position, rows) of the query tiles
+  // [win, win + 64) that see this key tile, one tile per lane: the walk reads
+  // them with readlane, without a memory round trip per tile.
+  int win = qb, rec_ql = 0, rec_qg = 0, rec_nr = 0;
+  auto load_window = [&](int w0) {
+    win = w0;
+    if (w0 + lane < qe) {
+      const int32_t* td = p.tiles + size_t(w0 + lane) * 8;
+      rec_ql = td[0];
+      rec_qg = td[1];
+      rec_nr = td[2];
+    }
   };
-  auto rows_of = [&](int t) { return p.tiles[size_t(t) * 8 + 2] * G; };
-  auto next_block = [&](Block b) -> Block {
-    if ((b.sb + 1) * kRowsPerBlock < rows_of(b.t)) return Block{b.t, b.sb + 1};
-    return Block{b.t + 1, 0};
+  if (qb < qe) load_window(qb);
+  auto load_tile = [&](int t) -> RowBlock {
+    RowBlock b{t, 0, 0, 0, 0};
+    if (t < qe) {
+      if (t - win >= 64) load_window(t);
+      const int idx = t - win;
+      b.qg = __builtin_amdgcn_readlane(rec_qg, idx);
+      b.nrg = __builtin_amdgcn_readlane(rec_nr, idx) * G;
+      b.base = size_t(__builtin_amdgcn_readlane(rec_ql, idx)) * hq + kvh * G;
+    }
+    return b;
   };
-  // Source row (index into [T_local * Hq]) of block row x; rows past the tile's
-  // end are clamped to its last row (and masked out by their query position).
-  auto src_row = [&](Block b, int x, int* qpos) -> size_t {
-    const int32_t* td = p.tiles + size_t(b.t) * 8;
-    const int n_r = td[2] * G;
-    const int ri = b.sb * kRowsPerBlock + x;
-    const int rc = min(ri, n_r - 1);
-    const int tok = rc / G;
-    if (qpos) *qpos = ri < n_r ? td[1] + tok : -1;
-    return size_t(td[0] + tok) * hq + kvh * G + (rc - tok * G);
+  auto next_block = [&](const RowBlock& b) -> RowBlock {
+    if (b.t >= qe) return b;
+    if ((b.sb + 1) * kRowsPerBlock < b.nrg) return RowBlock{b.t, b.sb + 1, b.qg, b.nrg, b.base};
+    return load_tile(b.t + 1);
   };
-  auto issue_block = [&](Block b, int slot) {
-    char* stage = ring + slot * S::STAGE;
+  // Row x of block b, as an offset from the tile's first row in [T_local * Hq]
+  // (token * Hq + head in group). Rows past the tile's end repeat its last row
+  // (the causal compare masks them out). Every factor is below 2^24.
+  auto row_off = [&](const RowBlock& b, int x) -> uint32_t {
+    const uint32_t rc = uint32_t(min(b.sb * kRowsPerBlock + x, b.nrg - 1)) & 127u;
+    const uint32_t tok = (rc * (opaque(ginv) & 0x1ffffu)) >> 16;
+    return rc + tok * (opaque(hq_minus_g) & 0xffffffu);   // tok * Hq + (rc - tok * G)
+  };
+  // When G divides 32, every block starts on a token, so in a block that lies
+  // wholly inside its tile row r is token r / G, head r % G of the block's first
+  // token: each lane's copy offsets are fixed for the whole walk and only a
+  // scalar base moves from block to block.
+  const bool aligned_blocks = kRowsPerBlock % G == 0;
+  const int tokens_per_block = kRowsPerBlock / G;
+  uint32_t qoff[S::Q_IPW], ooff[S::O_IPW];
+#pragma unroll
+  for (int i = 0; i < S::Q_IPW; ++i) {
+    const int q = (wave * S::Q_IPW + i) * 64 + lane;
+    const int r = q / S::KCPR;
+    const int c = (q - r * S::KCPR) ^ swz_kv<S::KCPR>(r);
+    qoff[i] = uint32_t(((r / G) * hq + r % G) * S::KROWB + c * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < S::O_IPW; ++i) {
+    const int q = (wave * S::O_IPW + i) * 64 + lane;
+    const int r = q / S::VCPR;
+    const int c = (q - r * S::VCPR) ^ swz_kv<S::VCPR>(r);
+    ooff[i] = uint32_t(((r / G) * hq + r % G) * S::VROWB + c * 16);
+  }
+  const uint32_t ioff = uint32_t((lane / G) * hq + lane % G);
+  // Each wave issues S::LOADS copies per block, waves 0 and 1 one more (the
+  // rows' lse2 and D).
+  auto issue_block = [&](const RowBlock& b, char* stage) {
+    const float* info = wave == 0 ? p.lse2 : p.delta;
+    char* info_lds = stage + S::INFO + wave * kRowsPerBlock * 4;
+    if (aligned_blocks && (b.sb + 1) * kRowsPerBlock <= b.nrg) {
+      const size_t rb = b.base + size_t(b.sb * tokens_per_block) * hq;
+      const char* qt = qbase + rb * S::KROWB;
+      const char* ot = obase + rb * S::VROWB;
+#pragma unroll
+      for (int i = 0; i < S::Q_IPW; ++i) load_lds16(qt + qoff[i], stage + (wave * S::Q_IPW + i) * 1024);
+#pragma unroll
+      for (int i = 0; i < S::O_IPW; ++i)
+        load_lds16(ot + ooff[i], stage + S::QBYTES + (wave * S::O_IPW + i) * 1024);
+      // gathered straight into LDS: a register load here would have to wait
+      // for every copy issued before it
+      if (wave < 2 && lane < kRowsPerBlock) load_lds4(reinterpret_cast<const char*>(info + rb + ioff), info_lds);
+      return;
+    }
+    const char* qt = qbase + b.base * S::KROWB;
+    const char* ot = obase + b.base * S::VROWB;
 #pragma unroll
     for (int i = 0; i < S::Q_IPW; ++i) {
       const int q = (wave * S::Q_IPW + i) * 64 + lane;
       const int r = q / S::KCPR;
-      const int c = (q - r * S::KCPR) ^ swz<S::KCPR>(r);
-      const char* src = qbase + src_row(b, r, nullptr) * S::KROWB + c * 16;
-      load_lds16(src, stage + (wave * S::Q_IPW + i) * 1024);
+      const int c = (q - r * S::KCPR) ^ swz_kv<S::KCPR>(r);
+      load_lds16(qt + (row_off(b, r) * S::KROWB + c * 16), stage + (wave * S::Q_IPW + i) * 1024);
     }
 #pragma unroll
     for (int i = 0; i < S::O_IPW; ++i) {
       const int q = (wave * S::O_IPW + i) * 64 + lane;
       const int r = q / S::VCPR;
-      const int c = (q - r * S::VCPR) ^ swz<S::VCPR>(r);
-      const char* src = obase + src_row(b, r, nullptr) * S::VROWB + c * 16;
-      load_lds16(src, stage + S::QBYTES + (wave * S::O_IPW + i) * 1024);
+      const int c = (q - r * S::VCPR) ^ swz_kv<S::VCPR>(r);
+      load_lds16(ot + (row_off(b, r) * S::VROWB + c * 16), stage + S::QBYTES + (wave * S::O_IPW + i) * 1024);
     }
-    if (wave == 0 && lane < kRowsPerBlock) {
-      int qpos;
-      const size_t sr = src_row(b, lane, &qpos);
-      float* rowinfo = reinterpret_cast<float*>(stage + S::QBYTES + S::OBYTES);
-      rowinfo[lane] = p.lse[sr] * kLog2e;
-      rowinfo[kRowsPerBlock + lane] = p.delta[sr];
-      reinterpret_cast<int*>(rowinfo)[2 * kRowsPerBlock + lane] = qpos;
+    if (wave < 2 && lane < kRowsPerBlock)
+      load_lds4(reinterpret_cast<const char*>(info + b.base + row_off(b, lane)), info_lds);
+  };
+  auto wait_block = [&](bool one_in_flight) {
+    if (!one_in_flight) {
+      wait_vmcnt<0>();
+    } else if (wave < 2) {
+      wait_vmcnt<S::LOADS + 1>();
+    } else {
+      wait_vmcnt<S::LOADS>();
     }
   };
 
-  f32x16 dk[S::DQB], dv[S::DVB];
+  f32x4 dk[S::KT], dv[S::VT];
 #pragma unroll
-  for (int b = 0; b < S::DQB; ++b) dk[b] = f32x16{};
+  for (int b = 0; b < S::KT; ++b) dk[b] = f32x4{};
 #pragma unroll
-  for (int b = 0; b < S::DVB; ++b) dv[b] = f32x16{};
+  for (int b = 0; b < S::VT; ++b) dv[b] = f32x4{};
 
-  const int key_rel = wave * 32 + lrow;            // this lane's key within the tile
-  const int key = ks + key_rel;
-  const bool key_ok = key_rel < nk;
   const float c2 = p.scale_log2;
-  const int tr_a = (lane & 15) >> 2;
-  const int tr_col = 16 * ((lane >> 4) & 1) + 4 * (lane & 3);
-  const char* kt_lds = kv_lds + key_rel * S::KROWB;
-  const char* vt_lds = kv_lds + S::KBYTES + key_rel * S::VROWB;
+  const int tr_row = 4 * grp + (lr >> 2);   // transposed reads: row within a 16-row half
+  const int tr_col = 4 * (lr & 3);
 
-  Block cur{qb, 0};
-  if (qb < qe) issue_block(cur, 0);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
-
-  for (int it = 0; cur.t < qe; ++it) {
-    const Block nxt = next_block(cur);
-    if (nxt.t < qe) issue_block(nxt, (it + 1) & 1);
-    const char* stage = ring + (it & 1) * S::STAGE;
-
-    // S = Q K^T and dP = dO V^T: lane holds key lane%32, rows 8(r/4) + 4*half + r%4.
-    f32x16 s = f32x16{}, dp = f32x16{};
+  // One row block: S = Q K^T and dP = dO V^T (lane: key lane%16, rows
+  // 16rt + 4*grp + i), P and dS as bf16 (hi, lo) pairs, then dV += P^T dO and
+  // dK += dS^T Q with k-slot 8*grp + j of the pairs holding row
+  // 16*(j/4) + 4*grp + j%4 and the B operands read transposed to match.
+  auto compute = [&](const char* stage, const RowBlock& b) {
+    f32x4 s[2] = {f32x4{}, f32x4{}}, dp[2] = {f32x4{}, f32x4{}};
 #pragma unroll
-    for (int st = 0; st < S::KSTEPS; ++st) {
-      const int ch = 2 * st + half;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + lrow * S::KROWB + ((ch ^ swz<S::KCPR>(lrow)) << 4));
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(kt_lds + ((ch ^ swz<S::KCPR>(key_rel)) << 4));
-      s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, s, 0, 0, 0);
-    }
+    for (int rt = 0; rt < 2; ++rt) {
+      const int r = 16 * rt + lr;
 #pragma unroll
-    for (int st = 0; st < S::VSTEPS; ++st) {
-      const int ch = 2 * st + half;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + S::QBYTES + lrow * S::VROWB + ((ch ^ swz<S::VCPR>(lrow)) << 4));
-      const bf16x8 b = *reinterpret_cast<const bf16x8*>(vt_lds + ((ch ^ swz<S::VCPR>(key_rel)) << 4));
-      dp = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, dp, 0, 0, 0);
-    }
-    const float* rowinfo = reinterpret_cast<const float*>(stage + S::QBYTES + S::OBYTES);
-    bf16x8 pt[2], ptl[2], dst[2], dsl[2];   // P and dS as bf16 pairs (hi + lo)
-#pragma unroll
-    for (int g = 0; g < 4; ++g) {
-      const int r0 = 8 * g + 4 * half;
-      const f32x4 l4 = *reinterpret_cast<const f32x4*>(rowinfo + r0);
-      const f32x4 d4 = *reinterpret_cast<const f32x4*>(rowinfo + kRowsPerBlock + r0);
-      const i32x4 q4 = *reinterpret_cast<const i32x4*>(rowinfo + 2 * kRowsPerBlock + r0);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = 4 * g + e;
-        float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[r], c2, -l4[e]));
-        if (!key_ok || key > q4[e]) pr = 0.0f;
-        const __bf16 phi = static_cast<__bf16>(pr);
-        pt[r >> 3][r & 7] = phi;
-        ptl[r >> 3][r & 7] = static_cast<__bf16>(pr - static_cast<float>(phi));
-        const float ds = pr * (dp[r] - d4[e]);
-        const __bf16 hi = static_cast<__bf16>(ds);
-        dst[r >> 3][r & 7] = hi;
-        dsl[r >> 3][r & 7] = static_cast<__bf16>(ds - static_cast<float>(hi));
+      for (int st = 0; st < (S::KS > S::VS ? S::KS : S::VS); ++st) {
+        if (st < S::KS) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              stage + r * S::KROWB + (((4 * st + grp) ^ swz_kv<S::KCPR>(r)) << 4));
+          s[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, kf[st], s[rt], 0, 0, 0);
+        }
+        if (st < S::VS) {
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+              stage + S::QBYTES + r * S::VROWB + (((4 * st + grp) ^ swz_kv<S::VCPR>(r)) << 4));
+          dp[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, vf[st], dp[rt], 0, 0, 0);
+        }
       }
     }
-    // dV += P^T dO and dK += dS^T Q; B operands: rows 16t + 4*half + {0..3, 8..11}.
+    // Rows of the block that see this lane's key: lo <= row < lo + span. Row
+    // ri = sb*32 + row of the tile sits at position qg + floor(ri / G), which
+    // is >= key exactly when ri >= (key - qg) * G; rows past the tile's rows
+    // see nothing.
+    const int kd_rel = min(max(key - b.qg, -1), 256);
+    const int lo = max(kd_rel * int(opaque(uint32_t(G)) & 0xffu) - b.sb * kRowsPerBlock, 0);
+    const int hi = min(b.nrg - b.sb * kRowsPerBlock, kRowsPerBlock);
+    const uint32_t span = uint32_t(max(hi - lo, 0));
+    const int row_bias = 4 * grp - lo;
+    const float* info = reinterpret_cast<const float*>(stage + S::INFO);
+    u32x4 ph, pl, dh, dl;
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int r0 = 16 * t + 4 * half + tr_a;
+    for (int rt = 0; rt < 2; ++rt) {
+      const int r0 = 16 * rt + 4 * grp;
+      const f32x4 l4 = *reinterpret_cast<const f32x4*>(info + r0);
+      const f32x4 d4 = *reinterpret_cast<const f32x4*>(info + kRowsPerBlock + r0);
+      float pr[4], ds[4];
 #pragma unroll
-      for (int b = 0; b < S::DVB; ++b) {
-        const int col = 32 * b + tr_col;
-        const bf16x8 o8 = tr_pair(stage + S::QBYTES, piece<S::VCPR, S::VROWB>(r0, col),
-                                  piece<S::VCPR, S::VROWB>(r0 + 8, col));
-        dv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(pt[t], o8, dv[b], 0, 0, 0);
-        dv[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ptl[t], o8, dv[b], 0, 0, 0);
+      for (int i = 0; i < 4; ++i) {
+        pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][i], c2, -l4[i]));
+        pr[i] = uint32_t(16 * rt + i + row_bias) < span ? pr[i] : 0.0f;
+        ds[i] = pr[i] * (dp[rt][i] - d4[i]);
       }
 #pragma unroll
-      for (int b = 0; b < S::DQB; ++b) {
-        const int col = 32 * b + tr_col;
-        const bf16x8 q8 = tr_pair(stage, piece<S::KCPR, S::KROWB>(r0, col),
-                                  piece<S::KCPR, S::KROWB>(r0 + 8, col));
-        dk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dst[t], q8, dk[b], 0, 0, 0);
-        dk[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(dsl[t], q8, dk[b], 0, 0, 0);
+      for (int i = 0; i < 4; i += 2) {
+        unsigned hw, lw;
+        split_pair(pr[i], pr[i + 1], hw, lw);
+        ph[2 * rt + i / 2] = hw;
+        pl[2 * rt + i / 2] = lw;
+        split_pair(ds[i], ds[i + 1], hw, lw);
+        dh[2 * rt + i / 2] = hw;
+        dl[2 * rt + i / 2] = lw;
       }
     }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    __syncthreads();
-    cur = nxt;
+    const bf16x8 pt = __builtin_bit_cast(bf16x8, ph), ptl = __builtin_bit_cast(bf16x8, pl);
+    const bf16x8 dst = __builtin_bit_cast(bf16x8, dh), dsl = __builtin_bit_cast(bf16x8, dl);
+#pragma unroll
+    for (int nt = 0; nt < S::VT; ++nt) {
+      const int col = 16 * nt + tr_col;
+      const bf16x8 o8 = tr_pair(stage + S::QBYTES, piece_kv<S::VCPR, S::VROWB>(tr_row, col),
+                                piece_kv<S::VCPR, S::VROWB>(16 + tr_row, col));
+      dv[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pt, o8, dv[nt], 0, 0, 0);
+      dv[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ptl, o8, dv[nt], 0, 0, 0);
+    }
+#pragma unroll
+    for (int nt = 0; nt < S::KT; ++nt) {
+      const int col = 16 * nt + tr_col;
+      const bf16x8 q8 = tr_pair(stage, piece_kv<S::KCPR, S::KROWB>(tr_row, col),
+                                piece_kv<S::KCPR, S::KROWB>(16 + tr_row, col));
+      dk[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dst, q8, dk[nt], 0, 0, 0);
+      dk[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(dsl, q8, dk[nt], 0, 0, 0);
+    }
+  };
+
+  if (qb < qe) {
+    // Walk: block i is computed from stage i % 3 while block i + 1 lands and
+    // block i + 2 is issued into the stage block i - 1 used.
+    RowBlock b0 = load_tile(qb);
+    RowBlock b1 = next_block(b0);
+    RowBlock b2 = next_block(b1);
+    issue_block(b0, stage0);
+    if (b1.t < qe) issue_block(b1, stage1);
+    wait_block(b1.t < qe);
+    lds_barrier();
+    auto step = [&](const char* cur, char* ahead) -> bool {
+      if (b0.t >= qe) return false;
+      const bool have2 = b2.t < qe;
+      if (have2) issue_block(b2, ahead);
+      const RowBlock b3 = next_block(b2);
+      compute(cur, b0);
+      wait_block(have2);
+      lds_barrier();
+      b0 = b1;
+      b1 = b2;
+      b2 = b3;
+      return true;
+    };
+    while (step(stage0, stage2) && step(stage1, stage0) && step(stage2, stage1)) {
+    }
   }
 
-  // Store: lane holds dims 32b + lane%32 of keys 32*wave + 8(r/4) + 4*half + r%4.
+  // Store: lane holds dims 16nt + lane%16 of keys 16*wave + 4*grp + i.
+  // All row indices are read before the first store (a store could alias them).
+  int grows[4];
 #pragma unroll
-  for (int r = 0; r < 16; ++r) {
-    const int kr = wave * 32 + 8 * (r >> 2) + 4 * half + (r & 3);
-    if (kr >= nk) continue;
-    const size_t grow = size_t(p.kv_row[ks + kr]) * hkv + kvh;
+  for (int i = 0; i < 4; ++i) {
+    const int kr = wave * kDkvKeysPerWave + 4 * grp + i;
+    grows[i] = kr < nk ? p.kv_row[ks + kr] : -1;
+  }
 #pragma unroll
-    for (int b = 0; b < S::DQB; ++b) p.dk[grow * DQK + 32 * b + lrow] = dk[b][r] * p.scale;
+  for (int i = 0; i < 4; ++i) {
+    if (grows[i] < 0) continue;
+    const size_t grow = size_t(grows[i]) * hkv + kvh;
 #pragma unroll
-    for (int b = 0; b < S::DVB; ++b) p.dv[grow * DV + 32 * b + lrow] = dv[b][r];
+    for (int nt = 0; nt < S::KT; ++nt) p.dk[grow * DQK + 16 * nt + lr] = dk[nt][i] * p.scale;
+#pragma unroll
+    for (int nt = 0; nt < S::VT; ++nt) p.dv[grow * DV + 16 * nt + lr] = dv[nt][i];
   }
 }
 
