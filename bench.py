@@ -14,6 +14,10 @@ Prints one JSON line. Besides the contract fields it carries
                 stream) against the dense bf16 MFMA peak, and the HBM traffic
                 per launch measured with rocprofv3 counters when the committed
                 counter summary matches the current kernel source;
+  timing        the forward kernel's median and minimum launch time with warm
+                caches and with cold caches (512 MiB written between launches),
+                and its median time for every rank of the configuration (same
+                tensors, that rank's metadata) with their max/min ratio;
   cpu_baseline  the fp64 oracle timed on this host's cores on the same
                 workload (reported, not a target).
 
@@ -181,7 +185,43 @@ def main(argv=None) -> int:
                      meta=meta, stream=stream)
         ends[i].record(stream)
     torch.cuda.synchronize()
-    kern_ms = float(np.mean([s.elapsed_time(e) for s, e in zip(starts, ends)]))
+    warm = [s.elapsed_time(e) for s, e in zip(starts, ends)]
+    kern_ms = float(np.mean(warm))
+
+    # Cold caches: a 512 MiB write (larger than L2 plus the 256 MB MALL)
+    # before each launch, on the same stream; median and minimum reported.
+    scratch = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    cold = []
+    for i in range(10):
+        scratch.fill_(i & 0xFF)
+        s0, s1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record(stream)
+        thd.attn_fwd(q=q, k=k, v=v, seqlens=batch.lengths, cp=w.cp, rank=w.rank, out=o, lse=lse,
+                     meta=meta, stream=stream)
+        s1.record(stream)
+        s1.synchronize()
+        cold.append(s0.elapsed_time(s1))
+    del scratch
+
+    # Every rank of the configuration on this GPU (same tensors, that rank's
+    # metadata): equal useful work per rank should give near-equal times, the
+    # one-GPU view of the partition's load balance.
+    per_rank = []
+    for r in range(w.cp):
+        meta_r = thd.device_metadata(seqlens=batch.lengths, cp=w.cp, rank=r, hq=w.hq, hkv=w.hkv,
+                                     d_qk=w.d_qk, d_v=w.d_v, device=0)
+        for _ in range(3):
+            thd.attn_fwd(q=q, k=k, v=v, seqlens=batch.lengths, cp=w.cp, rank=r, out=o, lse=lse,
+                         meta=meta_r, stream=stream)
+        evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(10)]
+        for s0, s1 in evs:
+            s0.record(stream)
+            thd.attn_fwd(q=q, k=k, v=v, seqlens=batch.lengths, cp=w.cp, rank=r, out=o, lse=lse,
+                         meta=meta_r, stream=stream)
+            s1.record(stream)
+        torch.cuda.synchronize()
+        per_rank.append(float(np.median([s0.elapsed_time(s1) for s0, s1 in evs])))
     # Algorithmic bytes per launch: Q once, every K/V row some local query sees
     # once (keys of document i up to the end of chunk 2cp-1-r), O and LSE once.
     seen_keys = sum((2 * w.cp - w.rank) * (int(L) // (2 * w.cp)) for L in batch.lengths)
@@ -220,6 +260,12 @@ def main(argv=None) -> int:
                    "useful_pairs": int(pairs), "backward": bool(w.backward)},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": roof,
+        "timing": {"fwd_kernel_ms_median_warm": round(float(np.median(warm)), 5),
+                   "fwd_kernel_ms_min_warm": round(float(np.min(warm)), 5),
+                   "fwd_kernel_ms_median_cold": round(float(np.median(cold)), 5),
+                   "fwd_kernel_ms_min_cold": round(float(np.min(cold)), 5),
+                   "fwd_kernel_ms_per_rank": [round(t, 5) for t in per_rank],
+                   "rank_spread": round(max(per_rank) / min(per_rank), 4)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = _cpu_baseline(w, batch)
