@@ -4,7 +4,8 @@ one context-parallel rank on one MI355X.
 A step is one pass of the whole path over one synthetic packed batch that is
 already resident in HBM: metadata lookup (cached after the first step, as the
 planner's cache is meant to be used), then the forward kernel (and, for the
-fwdbwd workload, the backward kernels). Useful FLOPs count only unmasked
+fwdbwd workload, the backward kernels, with the forward also writing its fp32
+O for the backward's D, as a training step would). Useful FLOPs count only unmasked
 (query, key) pairs: pairs x Hq x 2 (dqk + dv) forward, pairs x Hq x
 (6 dqk + 4 dv) backward.
 
@@ -137,14 +138,19 @@ def main(argv=None) -> int:
     o = torch.empty((w.t_local, w.hq, w.d_v), dtype=torch.bfloat16, device=dev)
     lse = torch.empty((w.t_local, w.hq), dtype=torch.float32, device=dev)
 
+    # Training step (fwdbwd): the forward also writes its fp32 O, from which
+    # the backward takes D (the path a training loop would use).
+    o32 = (torch.empty((w.t_local, w.hq, w.d_v), dtype=torch.float32, device=dev)
+           if w.backward else None)
+
     def step():
         meta = thd.device_metadata(seqlens=batch.lengths, cp=w.cp, rank=w.rank, hq=w.hq,
                                    hkv=w.hkv, d_qk=w.d_qk, d_v=w.d_v, device=0)
         thd.attn_fwd(q=q, k=k, v=v, seqlens=batch.lengths, cp=w.cp, rank=w.rank, out=o, lse=lse,
-                     meta=meta)
+                     out_f32=o32, meta=meta)
         if w.backward:
             thd.attn_bwd(q=q, k=k, v=v, lse=lse, d_o=do, seqlens=batch.lengths, cp=w.cp,
-                         rank=w.rank, meta=meta)
+                         rank=w.rank, o_f32=o32, meta=meta)
 
     # Parity gate: no throughput is reported for a path that disagrees with the oracle.
     step()

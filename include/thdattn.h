@@ -175,10 +175,15 @@ int thd_attn_fwd_workspace(const thd_meta* meta, int32_t hq, int32_t hkv, int32_
  * (192,128); Hq/Hkv <= 128. q, k, v, o, lse must be 16-byte aligned; k and v
  * must each be smaller than 4 GiB (THD_ERANGE otherwise). workspace (16-byte
  * aligned, at least thd_attn_fwd_workspace bytes; may be NULL when that is 0)
- * holds the split tiles' partial results; the forward allocates nothing. */
+ * holds the split tiles' partial results; the forward allocates nothing.
+ * o_f32 (optional, NULL to skip; fp32 [T_local, Hq, d_v], 16-byte aligned):
+ * when given, the probabilities enter the P.V product as bf16 (hi, lo) pairs
+ * and O is also written here in fp32, exact up to fp32 accumulation. It is
+ * meant for training: thd_attn_bwd then takes D = rowsum(dO * O) from it
+ * instead of recomputing D from the scores. */
 int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void* v,
-                 void* o, float* lse, int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
-                 float softmax_scale, void* workspace, int64_t workspace_bytes,
+                 void* o, float* lse, float* o_f32, int32_t hq, int32_t hkv, int32_t d_qk,
+                 int32_t d_v, float softmax_scale, void* workspace, int64_t workspace_bytes,
                  void* hip_stream);
 
 /* Bytes of device workspace thd_attn_bwd needs (caller allocates). */
@@ -187,12 +192,15 @@ int thd_attn_bwd_workspace(const thd_meta* meta, int32_t hq, int64_t* bytes);
 /* Backward: dq, and this rank's partial dk, dv (all fp32, layouts above),
  * from the forward's lse and the upstream gradient d_o. dk and dv are written
  * in full (zeros for keys no local query sees). The softmax-gradient term
- * D = rowsum(dO * O) is recomputed as rowsum(P * dP) from the scores, which is
- * equal for the exact O, so the forward's rounded o is not an input. The
- * workspace (size from thd_attn_bwd_workspace, 16-byte aligned) holds D and
- * the log-sum-exp in base 2 for every local row and q head. */
+ * D = rowsum(dO * O) needs O exact: it is taken from o_f32 (the forward's
+ * fp32 output, see thd_attn_fwd; 16-byte aligned) when that is not NULL, and
+ * otherwise recomputed as rowsum(P * dP) from the scores (one more pass over
+ * the keys), since the forward's bf16 o would make D's rounding the largest
+ * error in the gradients. The workspace (size from thd_attn_bwd_workspace,
+ * 16-byte aligned) holds D and the log-sum-exp in base 2 for every local row
+ * and q head. */
 int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void* v,
-                 const float* lse, const void* d_o,
+                 const float* lse, const float* o_f32, const void* d_o,
                  float* dq, float* dk, float* dv,
                  int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v, float softmax_scale,
                  void* workspace, int64_t workspace_bytes, void* hip_stream);

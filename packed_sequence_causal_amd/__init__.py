@@ -74,10 +74,10 @@ def _load():
         "thd_cache_clear": (ctypes.c_int, []),
         "thd_preferred_tiles": (ctypes.c_int, [i32, i32, i32, i32, pi32, pi32]),
         "thd_attn_fwd_workspace": (ctypes.c_int, [p, i32, i32, i32, pi64]),
-        "thd_attn_fwd": (ctypes.c_int, [p, p, p, p, p, p, i32, i32, i32, i32, ctypes.c_float, p, i64,
-                                        p]),
+        "thd_attn_fwd": (ctypes.c_int, [p, p, p, p, p, p, p, i32, i32, i32, i32, ctypes.c_float, p,
+                                        i64, p]),
         "thd_attn_bwd_workspace": (ctypes.c_int, [p, i32, pi64]),
-        "thd_attn_bwd": (ctypes.c_int, [p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
+        "thd_attn_bwd": (ctypes.c_int, [p, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
                                         ctypes.c_float, p, i64, p]),
     }
     for name, (res, args) in sigs.items():
@@ -242,11 +242,13 @@ def _workspace(device, nbytes: int):
 
 
 def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=None, lse=None,
-             stream=None, meta: Meta | None = None, concurrency: int | None = None):
+             out_f32=None, stream=None, meta: Meta | None = None, concurrency: int | None = None):
     """Forward attention for one rank. Returns (o bf16 [T_loc,Hq,dv], lse fp32 [T_loc,Hq]).
 
     q [T_loc, Hq, dqk], k [T, Hkv, dqk], v [T, Hkv, dv]: bf16 CUDA tensors,
     k/v already gathered rank-major. softmax_scale defaults to 1/sqrt(dqk).
+    out_f32 (optional fp32 [T_loc, Hq, dv] tensor) also receives O in fp32,
+    computed with split probabilities: pass it to attn_bwd as o_f32.
     """
     torch = _torch()
     hq, hkv, d_qk, d_v = q.shape[1], k.shape[1], q.shape[2], v.shape[2]
@@ -269,18 +271,24 @@ def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=No
     if lse is None:
         lse = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
     scale = 1.0 / math.sqrt(d_qk) if softmax_scale is None else float(softmax_scale)
+    if out_f32 is not None and (out_f32.dtype != torch.float32 or not out_f32.is_contiguous()
+                                or tuple(out_f32.shape) != (q.shape[0], hq, d_v)):
+        raise ThdError(-1, "out_f32 must be a contiguous fp32 [T_local, Hq, d_v] tensor")
     _check(_lib.thd_attn_fwd(meta.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                             out.data_ptr(), lse.data_ptr(), hq, hkv, d_qk, d_v, scale,
+                             out.data_ptr(), lse.data_ptr(),
+                             None if out_f32 is None else out_f32.data_ptr(),
+                             hq, hkv, d_qk, d_v, scale,
                              None if ws is None else ws.data_ptr(), need.value,
                              _stream_handle(stream, q.device)))
     return out, lse
 
 
 def attn_bwd(*, q, k, v, lse, d_o, seqlens, cp: int, rank: int, softmax_scale=None,
-             stream=None, meta: Meta | None = None, workspace=None):
+             o_f32=None, stream=None, meta: Meta | None = None, workspace=None):
     """Backward for one rank. Returns (dq fp32, dk fp32, dv fp32); dk/dv are
     this rank's partial sums in the gathered layout (zeros for unseen keys).
-    lse is the forward's; the forward's O is not needed."""
+    lse is the forward's. o_f32 (optional) is the forward's fp32 O from
+    attn_fwd(out_f32=...): D then comes from it instead of a pass over the keys."""
     torch = _torch()
     hq, hkv, d_qk, d_v = q.shape[1], k.shape[1], q.shape[2], v.shape[2]
     device = q.device.index
@@ -305,8 +313,12 @@ def attn_bwd(*, q, k, v, lse, d_o, seqlens, cp: int, rank: int, softmax_scale=No
         raise ThdError(-1, "lse must be a contiguous fp32 [T_local, Hq] tensor")
     if tuple(d_o.shape) != (q.shape[0], hq, d_v):
         raise ThdError(-5, "d_o must be [T_local, Hq, d_v]")
+    if o_f32 is not None and (o_f32.dtype != torch.float32 or not o_f32.is_contiguous()
+                              or tuple(o_f32.shape) != (q.shape[0], hq, d_v)):
+        raise ThdError(-1, "o_f32 must be a contiguous fp32 [T_local, Hq, d_v] tensor")
     _check(_lib.thd_attn_bwd(meta.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                             lse.data_ptr(), d_o.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                             lse.data_ptr(), None if o_f32 is None else o_f32.data_ptr(),
+                             d_o.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                              dv.data_ptr(), hq, hkv, d_qk, d_v, scale, workspace.data_ptr(),
                              workspace.numel(), _stream_handle(stream, q.device)))
     return dq, dk, dv

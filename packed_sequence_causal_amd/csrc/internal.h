@@ -81,6 +81,7 @@ struct FwdParams {
   const void* v;
   void* o;
   float* lse;
+  float* o_f32;       // optional fp32 copy of O (split P in the PV product); null to skip
   float* partial;     // workspace: per (part slot, kv head) O rows (fp32) then their lse
   const int32_t* tiles;
   const int32_t* items;
@@ -112,6 +113,7 @@ struct BwdParams {
   const void* k;
   const void* v;
   const float* lse;
+  const float* o_f32;   // optional exact O (fp32); D = rowsum(dO * O) from it when given
   const void* d_o;
   float* dq;
   float* dk;

@@ -352,7 +352,7 @@ int thd_attn_fwd_workspace(const thd_meta* meta, int32_t hq, int32_t hkv, int32_
 }
 
 int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void* v, void* o,
-                 float* lse, int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
+                 float* lse, float* o_f32, int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
                  float softmax_scale, void* workspace, int64_t workspace_bytes,
                  void* hip_stream) {
   return guarded([&] {
@@ -370,6 +370,7 @@ int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void*
     check_ptr(v, "v", 16);
     check_ptr(o, "o", 16);
     check_ptr(lse, "lse", 16);
+    if (o_f32 != nullptr) check_ptr(o_f32, "o_f32", 16);
     const int64_t need = p.n_part_slots * hkv * fwd_partial_floats(p.block_t, group, d_v) *
                          int64_t(sizeof(float));
     if (need > 0) {
@@ -388,6 +389,7 @@ int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void*
     fp.v = v;
     fp.o = o;
     fp.lse = lse;
+    fp.o_f32 = o_f32;
     fp.partial = static_cast<float*>(workspace);
     fp.tiles = d.tiles;
     fp.items = d.items;
@@ -415,7 +417,8 @@ int thd_attn_bwd_workspace(const thd_meta* meta, int32_t hq, int64_t* bytes) {
 }
 
 int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void* v,
-                 const float* lse, const void* d_o, float* dq, float* dk, float* dv, int32_t hq,
+                 const float* lse, const float* o_f32, const void* d_o, float* dq, float* dk,
+                 float* dv, int32_t hq,
                  int32_t hkv, int32_t d_qk, int32_t d_v, float softmax_scale, void* workspace,
                  int64_t workspace_bytes, void* hip_stream) {
   return guarded([&] {
@@ -432,6 +435,7 @@ int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void*
     check_ptr(k, "k", 16);
     check_ptr(v, "v", 16);
     check_ptr(lse, "lse", 16);
+    if (o_f32 != nullptr) check_ptr(o_f32, "o_f32", 16);
     check_ptr(d_o, "d_o", 16);
     check_ptr(dq, "dq", 16);
     check_ptr(dk, "dk", 16);
@@ -452,6 +456,7 @@ int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void*
     bp.k = k;
     bp.v = v;
     bp.lse = lse;
+    bp.o_f32 = o_f32;
     bp.d_o = d_o;
     bp.dq = dq;
     bp.dk = dk;

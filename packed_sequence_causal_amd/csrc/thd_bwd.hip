@@ -13,7 +13,9 @@
 // all-gather is a reduce-scatter of dK/dV, so this rank's dK/dV are partial
 // sums in the gathered layout.
 //
-// Three launches, no atomics (results are deterministic):
+// Three launches, no atomics (results are deterministic), or two when the
+// forward's exact fp32 O is given (dQ first, computing D = rowsum(dO * O) per
+// row from it, then dK/dV):
 //   1. thd_bwd_dq_kernel<delta = true>: D for every local row and q head;
 //   2. thd_bwd_dkdv_kernel (below);
 //   3. thd_bwd_dq_kernel<delta = false>: dQ. Both dQ-kernel passes run one
@@ -161,7 +163,35 @@ __global__ __launch_bounds__(kWaves * 64, DQK > 128 ? 1 : 2) void thd_bwd_dq_ker
       df[st] = valid ? *reinterpret_cast<const bf16x8*>(drow + 16 * st) : bf16x8{};
   }
   const float lse2 = valid ? p.lse[qrow_idx] * kLog2e : 0.0f;
-  const float dl = (!DELTA && valid) ? p.delta[qrow_idx] : 0.0f;
+  float dl = 0.0f;
+  if constexpr (!DELTA) {
+    if (p.o_f32 != nullptr) {
+      // D = rowsum(dO * O) from the forward's exact fp32 O: this lane's dims
+      // are those of its dO fragments, the other half's are in lane ^ 32.
+      // Written (with lse2) for the dK/dV kernel, which runs after this one.
+      float part = 0.0f;
+      if (valid) {
+        const float* orow = p.o_f32 + qrow_idx * DV + 8 * half;
+#pragma unroll
+        for (int st = 0; st < S::VSTEPS; ++st) {
+          const f32x4 a = *reinterpret_cast<const f32x4*>(orow + 16 * st);
+          const f32x4 b = *reinterpret_cast<const f32x4*>(orow + 16 * st + 4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            part = __builtin_fmaf(a[e], static_cast<float>(df[st][e]), part);
+            part = __builtin_fmaf(b[e], static_cast<float>(df[st][4 + e]), part);
+          }
+        }
+      }
+      dl = part + __shfl_xor(part, 32);
+      if (valid && half == 0) {
+        p.delta[qrow_idx] = dl;
+        p.lse2[qrow_idx] = lse2;
+      }
+    } else if (valid) {
+      dl = p.delta[qrow_idx];
+    }
+  }
   float dsum = 0.0f;   // delta pass: this lane's share of rowsum(P * dP)
 
   const char* __restrict__ kb = static_cast<const char*>(p.k);
@@ -671,11 +701,20 @@ template <int DQK, int DV>
 int launch(const BwdParams& p, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 q_grid(unsigned(int64_t(p.n_tiles) * p.hkv));
+  const dim3 kv_grid(unsigned(int64_t(p.n_kvtiles) * p.hkv));
+  hipError_t err;
+  if (p.o_f32 != nullptr) {
+    // dQ first: it computes D from the exact O and stores D and lse2.
+    hipLaunchKernelGGL((thd_bwd_dq_kernel<DQK, DV, false>), q_grid, dim3(kWaves * 64), 0, st, p);
+    err = hipGetLastError();
+    if (err != hipSuccess) return int(err);
+    hipLaunchKernelGGL((thd_bwd_dkdv_kernel<DQK, DV>), kv_grid, dim3(kDkvWaves * 64), 0, st, p);
+    return int(hipGetLastError());
+  }
   hipLaunchKernelGGL((thd_bwd_dq_kernel<DQK, DV, true>), q_grid, dim3(kWaves * 64), 0, st, p);
-  hipError_t err = hipGetLastError();
+  err = hipGetLastError();
   if (err != hipSuccess) return int(err);
-  hipLaunchKernelGGL((thd_bwd_dkdv_kernel<DQK, DV>), dim3(unsigned(int64_t(p.n_kvtiles) * p.hkv)),
-                     dim3(kDkvWaves * 64), 0, st, p);
+  hipLaunchKernelGGL((thd_bwd_dkdv_kernel<DQK, DV>), kv_grid, dim3(kDkvWaves * 64), 0, st, p);
   err = hipGetLastError();
   if (err != hipSuccess) return int(err);
   hipLaunchKernelGGL((thd_bwd_dq_kernel<DQK, DV, false>), q_grid, dim3(kWaves * 64), 0, st, p);

@@ -54,6 +54,9 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
@@ -74,6 +77,17 @@ constexpr int kWaitVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0)
 // host pass drop that kernel's launch stub.
 __device__ __forceinline__ void load_lds16(const char* src, char* lds) {
   __builtin_amdgcn_global_load_lds(src, (lds_void*)lds, 16, 0, 0);
+}
+
+// Splits (x0, x1) into two packed bf16 pairs: hi holds x truncated to bf16
+// (the upper half of each float, one byte permute), lo holds x - hi (exact in
+// fp32) rounded to bf16. hi + lo equals x to within 2^-16 of |x|.
+__device__ __forceinline__ void split_pair(float x0, float x1, unsigned& hi, unsigned& lo) {
+  const unsigned u0 = __builtin_bit_cast(unsigned, x0), u1 = __builtin_bit_cast(unsigned, x1);
+  hi = __builtin_amdgcn_perm(u1, u0, 0x07060302u);
+  const float r0 = x0 - __builtin_bit_cast(float, u0 & 0xffff0000u);
+  const float r1 = x1 - __builtin_bit_cast(float, u1 & 0xffff0000u);
+  lo = __builtin_bit_cast(unsigned, __builtin_convertvector(f32x2{r0, r1}, bf16x2));
 }
 
 // Position of 16-byte chunk c of LDS row r: c ^ swz(r). The XOR stays inside
@@ -113,7 +127,10 @@ struct FwdShape {
   static_assert(VCPR == 8 || VCPR == 16, "V chunk swizzle needs 8 or 16 chunks");
 };
 
-template <int DQK, int DV>
+// EXACT: P enters the PV product as a bf16 (hi, lo) pair and O is also written
+// in fp32 (p.o_f32): O is then exact up to fp32 accumulation, so the backward
+// can take D = rowsum(dO * O) from it.
+template <int DQK, int DV, bool EXACT>
 __global__ __launch_bounds__(kFwdThreads, 2) void thd_fwd_kernel(FwdParams p) {
   using S = FwdShape<DQK, DV>;
   constexpr int BN = S::BN;
@@ -279,7 +296,8 @@ __global__ __launch_bounds__(kFwdThreads, 2) void thd_fwd_kernel(FwdParams p) {
         }
       }
 
-      bf16x8 pb[RB][S::TS];
+      bf16x8 pb[RB][EXACT ? 1 : S::TS];
+      float neg_m_rb[RB];
 #pragma unroll
       for (int rb = 0; rb < RB; ++rb) {
         if (!rb_active[rb]) continue;
@@ -324,24 +342,55 @@ __global__ __launch_bounds__(kFwdThreads, 2) void thd_fwd_kernel(FwdParams p) {
         }
 
         const float neg_m = -m_run[rb];
+        neg_m_rb[rb] = neg_m;
         float ls[4] = {0.0f, 0.0f, 0.0f, 0.0f};   // independent partial sums
+        if constexpr (!EXACT) {
 #pragma unroll
-        for (int kb2 = 0; kb2 < S::KB; ++kb2)
+          for (int kb2 = 0; kb2 < S::KB; ++kb2)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][kb2][r], c2, neg_m));
-            ls[r & 3] += e;
-            pb[rb][2 * kb2 + (r >> 3)][r & 7] = static_cast<__bf16>(e);
-          }
+            for (int r = 0; r < 16; ++r) {
+              const float e = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][kb2][r], c2, neg_m));
+              ls[r & 3] += e;
+              pb[rb][2 * kb2 + (r >> 3)][r & 7] = static_cast<__bf16>(e);
+            }
+        }
         l_run[rb] += (ls[0] + ls[1]) + (ls[2] + ls[3]);
       }
 
       // O^T += V^T P^T, 16 keys per MFMA: keys 16t + 4*half + {0..3, 8..11};
-      // each V^T fragment feeds every row block.
+      // each V^T fragment feeds every row block. EXACT computes each 16-key
+      // step's P here (exp, then the bf16 pair split) so that only one step's
+      // pairs are live at a time.
 #pragma unroll
       for (int t = 0; t < S::TS; ++t) {
         const int r0 = 16 * t + 4 * half + tr_a;
         const int r1 = r0 + 8;
+        bf16x8 p_hi[RB], p_lo[RB];
+        if constexpr (EXACT) {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) {
+            if (!rb_active[rb]) continue;
+            u32x4 hw4, lw4;
+            float lsum = 0.0f;
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+              const int r = 8 * (t & 1) + i;
+              const float e0 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][t >> 1][r], c2, neg_m_rb[rb]));
+              const float e1 = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rb][t >> 1][r + 1], c2, neg_m_rb[rb]));
+              lsum += e0 + e1;
+              unsigned hw, lw;
+              split_pair(e0, e1, hw, lw);
+              hw4[i >> 1] = hw;
+              lw4[i >> 1] = lw;
+            }
+            l_run[rb] += lsum;
+            p_hi[rb] = __builtin_bit_cast(bf16x8, hw4);
+            p_lo[rb] = __builtin_bit_cast(bf16x8, lw4);
+          }
+        } else {
+#pragma unroll
+          for (int rb = 0; rb < RB; ++rb) p_hi[rb] = pb[rb][t];
+        }
 #pragma unroll
         for (int b = 0; b < S::DVB; ++b) {
           const int dv = 32 * b + tr_dv;
@@ -351,8 +400,12 @@ __global__ __launch_bounds__(kFwdThreads, 2) void thd_fwd_kernel(FwdParams p) {
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + off1));
           const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            if (rb_active[rb]) acc[rb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pb[rb][t], acc[rb][b], 0, 0, 0);
+          for (int rb = 0; rb < RB; ++rb) {
+            if (!rb_active[rb]) continue;
+            acc[rb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p_hi[rb], acc[rb][b], 0, 0, 0);
+            if constexpr (EXACT)
+              acc[rb][b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p_lo[rb], acc[rb][b], 0, 0, 0);
+          }
         }
       }
     }
@@ -394,15 +447,21 @@ __global__ __launch_bounds__(kFwdThreads, 2) void thd_fwd_kernel(FwdParams p) {
       if (half == 0) base[size_t(rows) * DV + row] = m_run[rb] + __builtin_amdgcn_logf(l_tot);
       continue;
     }
-    __bf16* orow = static_cast<__bf16*>(p.o) + (size_t(q_local0 + tok[rb]) * p.hq + head[rb]) * DV;
+    const size_t orow_idx = size_t(q_local0 + tok[rb]) * p.hq + head[rb];
+    __bf16* orow = static_cast<__bf16*>(p.o) + orow_idx * DV;
 #pragma unroll
     for (int b = 0; b < S::DVB; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        f32x4 o4;
         bf16x4 out;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) out[e] = static_cast<__bf16>(acc[rb][b][4 * g + e] * inv);
+        for (int e = 0; e < 4; ++e) {
+          o4[e] = acc[rb][b][4 * g + e] * inv;
+          out[e] = static_cast<__bf16>(o4[e]);
+        }
         *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * g + 4 * half) = out;
+        if constexpr (EXACT) *reinterpret_cast<f32x4*>(p.o_f32 + orow_idx * DV + 32 * b + 8 * g + 4 * half) = o4;
       }
     if (half == 0)
       p.lse[size_t(q_local0 + tok[rb]) * p.hq + head[rb]] = (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
@@ -451,9 +510,14 @@ __global__ __launch_bounds__(256) void thd_fwd_combine_kernel(FwdParams p) {
   const int head = kvh * G + (row - tok * G);
   const size_t orow = size_t(td[0] + tok) * p.hq + head;
   bf16x4 out;
+  f32x4 o4;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) out[e] = static_cast<__bf16>(acc[e] * inv);
+  for (int e = 0; e < 4; ++e) {
+    o4[e] = acc[e] * inv;
+    out[e] = static_cast<__bf16>(o4[e]);
+  }
   *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.o) + orow * DV + col) = out;
+  if (p.o_f32 != nullptr) *reinterpret_cast<f32x4*>(p.o_f32 + orow * DV + col) = o4;
   if (col == 0) p.lse[orow] = (mx + __builtin_amdgcn_logf(wsum)) * kLn2;
 }
 
@@ -461,7 +525,11 @@ template <int DQK, int DV>
 int launch(const FwdParams& p, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid(unsigned(int64_t(p.n_items) * p.hkv));
-  hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV>), grid, dim3(kFwdThreads), 0, st, p);
+  if (p.o_f32 != nullptr) {
+    hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV, true>), grid, dim3(kFwdThreads), 0, st, p);
+  } else {
+    hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV, false>), grid, dim3(kFwdThreads), 0, st, p);
+  }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.n_splits == 0) return int(err);
   const int64_t threads = int64_t(p.n_splits) * p.hkv * p.block_t * p.group * (DV / 4);

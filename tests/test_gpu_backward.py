@@ -20,16 +20,21 @@ pytestmark = pytest.mark.gpu
 thd = pytest.importorskip("packed_sequence_causal_amd")
 
 
-def _run(batch, rank=None, scale=None):
+def _run(batch, rank=None, scale=None, exact_o=False):
+    """Forward then backward on the GPU. exact_o: the forward also writes its
+    fp32 O and the backward takes D from it (two backward launches instead of
+    three)."""
     w = batch.workload
     r = w.rank if rank is None else rank
     dev = device()
     q, k, v, do = (t.to(dev) for t in (batch.q, batch.k, batch.v, batch.do))
     print(f"[bwd] case={w.name} n={len(batch.lengths)} cp={w.cp} rank={r} hq={w.hq} hkv={w.hkv} "
-          f"dqk={w.d_qk} dv={w.d_v}", flush=True)
-    o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=batch.lengths, cp=w.cp, rank=r, softmax_scale=scale)
+          f"dqk={w.d_qk} dv={w.d_v} exact_o={exact_o}", flush=True)
+    o32 = torch.empty((q.shape[0], w.hq, w.d_v), dtype=torch.float32, device=dev) if exact_o else None
+    o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=batch.lengths, cp=w.cp, rank=r, softmax_scale=scale,
+                          out_f32=o32)
     dq, dk, dv = thd.attn_bwd(q=q, k=k, v=v, lse=lse, d_o=do, seqlens=batch.lengths, cp=w.cp,
-                              rank=r, softmax_scale=scale)
+                              rank=r, softmax_scale=scale, o_f32=o32)
     torch.cuda.synchronize()
     return dq, dk, dv
 
@@ -61,24 +66,40 @@ SMALL = [
 ]
 
 
+@pytest.mark.parametrize("exact_o", [False, True], ids=["D_from_scores", "D_from_o32"])
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: f"seed{c[0]}")
-def test_backward_matches_oracle_small(case):
+def test_backward_matches_oracle_small(case, exact_o):
     seed, lengths, cp, rank, hq, hkv, dqk, dv = case
     b = workloads.small_case(seed, lengths, cp, hq, hkv, dqk, dv, backward=True, rank=rank)
-    got = _run(b)
+    got = _run(b, exact_o=exact_o)
     _check(b, got)
 
 
-def test_backward_custom_scale():
+@pytest.mark.parametrize("exact_o", [False, True], ids=["D_from_scores", "D_from_o32"])
+def test_backward_custom_scale(exact_o):
     b = workloads.small_case(58, [64, 192], 2, 8, 2, 128, 128, backward=True, rank=1)
-    got = _run(b, scale=0.2)
+    got = _run(b, scale=0.2, exact_o=exact_o)
     _check(b, got, scale=0.2)
 
 
-def test_backward_fwdbwd_workload_full():
+def test_backward_paths_agree():
+    """D from the scores and D from the exact fp32 O give the same gradients
+    up to fp32 rounding."""
+    b = workloads.small_case(53, [16 * x for x in (1, 2, 3, 5, 8, 13, 21, 32)], 8, 64, 8, 128, 128,
+                             backward=True, rank=0)
+    g0 = _run(b, exact_o=False)
+    g1 = _run(b, exact_o=True)
+    for name, a, c in zip(("dQ", "dK", "dV"), g0, g1):
+        diff = (a - c).abs().max().item()
+        print(f"[bwd] paths {name} max diff {diff:.3g}", flush=True)
+        assert diff <= 1e-4
+
+
+@pytest.mark.parametrize("exact_o", [False, True], ids=["D_from_scores", "D_from_o32"])
+def test_backward_fwdbwd_workload_full(exact_o):
     w = workloads.BY_NAME["fwdbwd"]
     b = workloads.make_batch(w)
-    dq, dk, dv = _run(b)
+    dq, dk, dv = _run(b, exact_o=exact_o)
     _check(b, (dq, dk, dv))
     # keys no local query sees (offsets >= (2cp - r) c in each document) are exact zeros
     cu = opart.cu_seqlens(b.lengths)
@@ -89,7 +110,7 @@ def test_backward_fwdbwd_workload_full():
     idx = torch.from_numpy(unseen).to(dk.device)
     assert torch.count_nonzero(dk[idx]).item() == 0 and torch.count_nonzero(dv[idx]).item() == 0
     # bitwise reproducible (no atomics)
-    dq2, dk2, dv2 = _run(b)
+    dq2, dk2, dv2 = _run(b, exact_o=exact_o)
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
 
 

@@ -94,6 +94,42 @@ def test_forward_split_key_ranges_match_oracle(case, concurrency):
     assert (lse - lse1).abs().max().item() <= 1e-4
 
 
+EXACT = [
+    # (seed, lengths, cp, rank, hq, hkv, dqk, dv, concurrency)
+    (81, [256, 512, 256], 2, 0, 8, 8, 64, 64, 0),
+    (82, [8, 24, 40, 136, 520], 4, 1, 32, 8, 128, 128, 0),
+    (83, [16, 32, 1040, 16, 400], 8, 3, 16, 16, 192, 128, 0),
+    (84, [2048, 512, 1024], 2, 1, 16, 4, 128, 128, 64),    # split key ranges: combine writes O32
+    (85, [36, 300, 84], 3, 2, 12, 4, 128, 128, 0),
+]
+O32_ABS = 2e-4   # split probabilities: O limited by fp32 accumulation
+
+
+@pytest.mark.parametrize("case", EXACT, ids=lambda c: f"seed{c[0]}")
+def test_forward_fp32_output_is_exact(case):
+    """With out_f32, P enters P.V as a bf16 pair: the fp32 O matches the fp64
+    oracle far inside the bf16 tolerance, and o and lse still match."""
+    seed, lengths, cp, rank, hq, hkv, dqk, dv, conc = case
+    b = workloads.small_case(seed, lengths, cp, hq, hkv, dqk, dv, rank=rank)
+    dev = device()
+    q, k, v = b.q.to(dev), b.k.to(dev), b.v.to(dev)
+    print(f"[fwd] exact case seed={seed} cp={cp} rank={rank} dqk={dqk} concurrency={conc}", flush=True)
+    meta = thd.device_metadata(seqlens=b.lengths, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=dqk,
+                               d_v=dv, device=0, concurrency=conc)
+    o32 = torch.full((q.shape[0], hq, dv), float("nan"), dtype=torch.float32, device=dev)
+    o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=b.lengths, cp=cp, rank=rank, out_f32=o32,
+                          meta=meta)
+    torch.cuda.synchronize()
+    want_o, want_lse = oatt.attn_fwd64(to64(b.q), to64(b.k), to64(b.v), lengths, cp, rank)
+    assert_close(to64(o), want_o, "O")
+    assert_close(lse.cpu().double().numpy(), want_lse, "LSE", max_abs=LSE_ABS, mean_abs=LSE_ABS)
+    err = np.abs(o32.cpu().double().numpy() - want_o)
+    print(f"[fwd] O32 max-abs {err.max():.3g} mean-abs {err.mean():.3g}", flush=True)
+    assert err.max() <= O32_ABS
+    # the bf16 output is the fp32 one rounded to nearest even
+    assert torch.equal(o, o32.to(torch.bfloat16))
+
+
 def test_forward_custom_scale():
     b = workloads.small_case(21, [64, 192], 2, 8, 2, 128, 128, rank=1)
     o, lse = _run(b, scale=0.3)

@@ -132,8 +132,8 @@ def test_null_pointers_return_errors():
     assert lib.thd_meta_info(None, None) == -1
     assert lib.thd_meta_copy(None, 0, None, 0) == -1
     lib.thd_meta_release(None)
-    assert lib.thd_attn_fwd(None, None, None, None, None, None, 1, 1, 128, 128, 1.0, None, 0,
-                            None) == -1
+    assert lib.thd_attn_fwd(None, None, None, None, None, None, None, 1, 1, 128, 128, 1.0, None,
+                            0, None) == -1
     assert b"NULL" in lib.thd_last_error()
     m = thd.build_metadata(seqlens=[8], cp=1, rank=0, block_t=4, block_n=64)
     n = ctypes.c_int32()
@@ -147,7 +147,7 @@ def test_forward_rejects_host_only_metadata_and_bad_arguments():
     buf = ctypes.create_string_buffer(1 << 16)
     ptr = (ctypes.addressof(buf) + 15) // 16 * 16
     lib = thd._lib
-    args = [m.handle, ptr, ptr, ptr, ptr, ptr]
+    args = [m.handle, ptr, ptr, ptr, ptr, ptr, None]
     tail = [None, 0, None]
     # unsupported head dims are refused before any device check
     assert lib.thd_attn_fwd(*args, 32, 8, 96, 96, 0.1, *tail) == -8
@@ -157,14 +157,19 @@ def test_forward_rejects_host_only_metadata_and_bad_arguments():
     # tile sizes that do not fit the group size
     assert lib.thd_attn_fwd(*args, 64, 8, 128, 128, 0.1, *tail) == -5
     # misaligned pointer
-    assert lib.thd_attn_fwd(m.handle, ptr + 2, ptr, ptr, ptr, ptr, 32, 8, 128, 128, 0.1, *tail) == -4
+    assert lib.thd_attn_fwd(m.handle, ptr + 2, ptr, ptr, ptr, ptr, None, 32, 8, 128, 128, 0.1,
+                            *tail) == -4
+    # misaligned optional fp32 output
+    assert lib.thd_attn_fwd(m.handle, ptr, ptr, ptr, ptr, ptr, ptr + 4, 32, 8, 128, 128, 0.1,
+                            *tail) == -4
     # host-only metadata cannot launch
     assert lib.thd_attn_fwd(*args, 32, 8, 128, 128, 0.1, *tail) == -5
     assert b"device" in lib.thd_last_error()
     # a split plan needs its workspace
     ms = thd.build_metadata(seqlens=[4096], cp=1, rank=0, block_t=32, block_n=64, concurrency=256)
     assert ms.info()["n_part_slots"] > 0
-    assert lib.thd_attn_fwd(ms.handle, ptr, ptr, ptr, ptr, ptr, 32, 8, 128, 128, 0.1, *tail) == -1
+    assert lib.thd_attn_fwd(ms.handle, ptr, ptr, ptr, ptr, ptr, None, 32, 8, 128, 128, 0.1,
+                            *tail) == -1
     assert b"workspace" in lib.thd_last_error()
 
 
