@@ -268,24 +268,37 @@ __global__ __launch_bounds__(kWaves * 64, DQK > 128 ? 1 : 2) void thd_bwd_dq_ker
       }
       const bool masked = j >= n_full;
       const int key0 = kv_start + j * BN + 4 * half;
-      // dS as a bf16 pair (hi + lo): its rounding stays ~2^-17 relative.
-      bf16x8 dsb[4], dsl[4];
+      // dS as a bf16 pair (hi + lo): its rounding stays ~2^-16 relative.
+      u32x4 dsh4[4], dsl4[4];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int key = key0 + 32 * kb2 + 8 * (r >> 2) + (r & 3);
-          float pr = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r], c2, -lse2));
-          if (masked && key > qpos) pr = 0.0f;
-          if constexpr (DELTA) {
-            dsum = __builtin_fmaf(pr, dp[kb2][r], dsum);
-          } else {
-            const float ds = pr * (dp[kb2][r] - dl);
-            const __bf16 hi = static_cast<__bf16>(ds);
-            dsb[2 * kb2 + (r >> 3)][r & 7] = hi;
-            dsl[2 * kb2 + (r >> 3)][r & 7] = static_cast<__bf16>(ds - static_cast<float>(hi));
+        for (int r = 0; r < 16; r += 2) {
+          float pr[2], ds[2];
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int key = key0 + 32 * kb2 + 8 * ((r + e) >> 2) + ((r + e) & 3);
+            pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r + e], c2, -lse2));
+            if (masked && key > qpos) pr[e] = 0.0f;
+            if constexpr (DELTA) {
+              dsum = __builtin_fmaf(pr[e], dp[kb2][r + e], dsum);
+            } else {
+              ds[e] = pr[e] * (dp[kb2][r + e] - dl);
+            }
+          }
+          if constexpr (!DELTA) {
+            unsigned hw, lw;
+            split_pair(ds[0], ds[1], hw, lw);
+            dsh4[2 * kb2 + (r >> 3)][(r & 7) >> 1] = hw;
+            dsl4[2 * kb2 + (r >> 3)][(r & 7) >> 1] = lw;
           }
         }
+      bf16x8 dsb[4], dsl[4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        dsb[t] = __builtin_bit_cast(bf16x8, dsh4[t]);
+        dsl[t] = __builtin_bit_cast(bf16x8, dsl4[t]);
+      }
       // dQ^T += K^T dS^T: K^T rows (dims) 32b + lane%32, keys 16t + 4*half + {0..3, 8..11}.
 #pragma unroll
       for (int t = 0; t < (DELTA ? 0 : 4); ++t) {
