@@ -53,6 +53,39 @@ def build(verbose: bool = False) -> str:
     return LIB
 
 
+def resources() -> str:
+    """Per-kernel register, LDS and scratch use of the gfx950 code (read from
+    the assembler's kernel descriptors), as a Markdown table."""
+    import re
+    rows = []
+    for src in SOURCES:
+        if not src.endswith(".hip"):
+            continue
+        asm = os.path.join(BUILD, os.path.splitext(src)[0] + ".s")
+        os.makedirs(BUILD, exist_ok=True)
+        cmd = [HIPCC] + COMMON + DEVICE + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm]
+        res = subprocess.run(cmd, capture_output=True, text=True)
+        if res.returncode != 0:
+            raise RuntimeError(res.stderr)
+        text = open(asm).read()
+        for name, body in re.findall(r"\.amdhsa_kernel (\S+)(.*?)\.end_amdhsa_kernel", text, re.S):
+            def field(key):
+                m = re.search(r"\.amdhsa_" + key + r" (\d+)", body)
+                return int(m.group(1)) if m else 0
+            vgpr, acc = field("next_free_vgpr"), field("accum_offset")
+            lds, scratch, sgpr = field("group_segment_fixed_size"), field("private_segment_fixed_size"), field("next_free_sgpr")
+            demangled = subprocess.run(["c++filt", name], capture_output=True, text=True).stdout.strip()
+            short = re.sub(r"thd::\(anonymous namespace\)::", "", demangled).replace("(thd::FwdParams)", "").replace("(thd::BwdParams)", "")
+            waves = max(1, min(8, 512 // max(vgpr, 1)))
+            rows.append(f"| `{short}` | {vgpr} | {max(vgpr - acc, 0)} | {sgpr} | {lds} | {scratch} | {waves} |")
+    head = ("| kernel | VGPRs (arch + acc) | of which AGPRs | SGPRs | LDS bytes | scratch bytes | waves per SIMD by VGPRs |\n"
+            "|---|---|---|---|---|---|---|")
+    return head + "\n" + "\n".join(rows)
+
+
 if __name__ == "__main__":
+    if "--resources" in sys.argv:
+        print(resources())
+        sys.exit(0)
     build(verbose=True)
     sys.exit(0)

@@ -1,0 +1,13 @@
+// Kernel-launcher stand-ins for host-only builds of the library's planner and
+// C ABI (the sanitizer test links these instead of the HIP kernels): every
+// launch reports an error, and no kernel shape is supported.
+#include <hip/hip_runtime_api.h>
+
+#include "internal.h"
+
+namespace thd {
+int launch_fwd(const FwdParams&, int, int, void*) { return int(hipErrorInvalidValue); }
+int launch_bwd(const BwdParams&, int, int, void*) { return int(hipErrorInvalidValue); }
+bool fwd_supported(int, int) { return false; }
+bool bwd_supported(int, int) { return false; }
+}  // namespace thd
