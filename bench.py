@@ -231,8 +231,11 @@ def main(argv=None) -> int:
     # Algorithmic bytes per launch: Q once, every K/V row some local query sees
     # once (keys of document i up to the end of chunk 2cp-1-r), O and LSE once.
     seen_keys = sum((2 * w.cp - w.rank) * (int(L) // (2 * w.cp)) for L in batch.lengths)
+    # Q, every visible K/V row once, O (bf16, plus the fp32 copy the training
+    # forward writes for the backward), LSE.
+    o_bytes = (2 + (4 if w.backward else 0)) * w.t_local * w.hq * w.d_v
     alg_bytes = (2 * w.t_local * w.hq * w.d_qk + 2 * w.hkv * (w.d_qk + w.d_v) * seen_keys
-                 + 2 * w.t_local * w.hq * w.d_v + 4 * w.t_local * w.hq)
+                 + o_bytes + 4 * w.t_local * w.hq)
     intensity = fwd_flops / alg_bytes
     ridge = PEAK_BF16_TFLOPS * 1e12 / (PEAK_HBM_GBS * 1e9)
     traffic = _traffic(w.name)
