@@ -62,7 +62,7 @@ typedef enum {
 } thd_status;
 
 /* Version of the tile-table contract (the per-tile bounds and work items below). */
-#define THD_META_VERSION 2
+#define THD_META_VERSION 3
 
 /* Fields of a metadata object, for thd_meta_copy. All int32.
  *   Q_GLOBAL  [T_local]       global packed position of each local query row
@@ -84,6 +84,9 @@ typedef enum {
  *                             the tile is not split)
  *   SPLITS    [n_splits*4]    tiles whose key range is split: tile, first part
  *                             slot, number of parts, 0
+ *   DOC_END   [n_docs]        global position one past each document's last
+ *                             real token (cu_i + L_i without padding; see
+ *                             thd_build_metadata_padded)
  * With concurrency C > 0 (work items of one kv head the device runs at once)
  * and fewer than 2C tiles, the key range of tiles longer than
  * kv_split = max(ceil(sum of n_kv_tiles / C), 8) KV tiles is cut into
@@ -98,7 +101,8 @@ enum {
   THD_FIELD_ORDER = 4,
   THD_FIELD_KVTILES = 5,
   THD_FIELD_ITEMS = 6,
-  THD_FIELD_SPLITS = 7
+  THD_FIELD_SPLITS = 7,
+  THD_FIELD_DOC_END = 8
 };
 
 typedef struct thd_meta thd_meta;   /* opaque, library-owned, reference-counted */
@@ -113,6 +117,7 @@ typedef struct {
   int64_t n_items;          /* forward work items */
   int64_t n_splits;         /* tiles whose key range is split */
   int64_t n_part_slots;     /* partial-result slots (sum of parts over split tiles) */
+  int64_t pad_tokens;       /* pad tokens over all documents (0 without padding) */
   int32_t concurrency, kv_split;
   int32_t n_docs, cp, rank, block_t, block_n, version;
   int32_t device;           /* device holding the uploaded copy, -1 = host only */
@@ -143,6 +148,28 @@ int thd_plan_partition(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32
 int thd_build_metadata(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank,
                        int32_t block_t, int32_t block_n, int32_t concurrency, int32_t device,
                        thd_meta** out);
+
+/* Padding-tolerant partitioning (relaxes the divisibility rule above). A
+ * document of R_i >= 1 real tokens is stored padded to
+ * L_i = ceil(R_i / (2*cp)) * 2*cp tokens: its R_i real tokens first, then
+ * L_i - R_i pad tokens (any finite values). The padded batch is partitioned,
+ * gathered and laid out exactly like an unpadded one of lengths L_i
+ * (thd_plan_partition with those lengths gives the maps). Pads follow every real token of their
+ * document, so the causal mask already hides them from real queries: real rows
+ * get exactly the attention of the unpadded documents. Pad rows get O = 0 and
+ * LSE = +inf (so exp(S - LSE) = 0: the backward gives pad rows dQ = 0 whatever
+ * dO holds there, and pad keys dK = dV = 0).
+ * thd_pad_lengths writes L_i into padded[n_docs] (host). Errors: THD_EINVAL
+ * (NULL pointer, n_docs < 1, a length < 1), THD_ERANGE (cp < 1 or a padded
+ * length beyond int32). */
+int thd_pad_lengths(const int32_t* real_lengths, int32_t n_docs, int32_t cp, int32_t* padded);
+
+/* thd_build_metadata for the padded layout of real_lengths[n_docs] (host):
+ * the arrays of the padded lengths L_i, plus DOC_END = cu_i + R_i. The cache
+ * key holds the real lengths. */
+int thd_build_metadata_padded(const int32_t* real_lengths, int32_t n_docs, int32_t cp,
+                              int32_t rank, int32_t block_t, int32_t block_n,
+                              int32_t concurrency, int32_t device, thd_meta** out);
 
 int thd_meta_info(const thd_meta* meta, thd_meta_info_t* info);
 

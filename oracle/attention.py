@@ -166,6 +166,35 @@ def attn_bwd64(q, k, v, do, seqlens, cp, rank, scale=None):
     return dq, dk, dv
 
 
+def attn_fwd64_padded(q, k, v, real_lengths, cp, rank, scale=None):
+    """Forward over the padded layout of partition.pad_lengths (fp64).
+
+    Real rows: the attention above over their document's keys cu_i .. g, all
+    real (pads follow every real token). Pad rows (a reading; the pages have no
+    padding): O = 0 and LSE = +inf, the log-sum-exp that makes exp(S - LSE)
+    vanish, so that a backward built on P = exp(S - LSE) gives them nothing.
+    """
+    lengths = partition.pad_lengths(real_lengths, cp)
+    out, lse = attn_fwd64(q, k, v, lengths, cp, rank, scale)
+    pad = partition.pad_rows(real_lengths, cp, rank)
+    out[pad] = 0.0
+    lse[pad] = np.inf
+    return out, lse
+
+
+def attn_bwd64_padded(q, k, v, do, real_lengths, cp, rank, scale=None):
+    """Backward over the padded layout: pad rows take part with P = 0.
+
+    With P = 0 on a pad row its dS is 0 whatever dO holds there, so it adds
+    nothing to dK, dV and gets dQ = 0; pad keys are seen by no real row and get
+    exact zeros. That is the backward above with dO zeroed on pad rows.
+    """
+    lengths = partition.pad_lengths(real_lengths, cp)
+    do = np.array(do, dtype=np.float64)
+    do[partition.pad_rows(real_lengths, cp, rank)] = 0.0
+    return attn_bwd64(q, k, v, do, lengths, cp, rank, scale)
+
+
 def brute_fwd(q, k, v, seqlens, cp, rank, scale=None):
     """Pure Python loops over (row, head, key, dim); tiny inputs only.
 

@@ -5,7 +5,7 @@ Test infrastructure only (see the package docstring).
 The subject page ("kvallgather cp thd load balance", section "What this PR does
 / why we need it?") says metadata is cached to avoid repeated computation but
 gives no format. The format below is this project's interface contract between
-the host planner and the GPU kernels (version 2). It is unique given
+the host planner and the GPU kernels (version 3). It is unique given
 (lengths, cp, rank, BT, BN, concurrency), so the host library must reproduce it bit for bit.
 
 Definitions (all integer, floor division of non-negative values):
@@ -19,6 +19,11 @@ k = r for s = 0, k = 2cp-1-r for s = 1), token offsets t0 = 0, BT, 2BT, ... < c_
     n_full  = (q_glob - cu_i + 1) // BN            (KV tiles every row sees whole)
     record  = [cu_i/cp + s*c_i + t0, q_glob, n_rows, i, s, cu_i, n_kv, n_full]
 KV tile j of a Q tile covers keys [cu_i + j*BN, cu_i + min((j+1)*BN, kv_len)).
+
+doc_end[n_docs] (version 3): global position one past the last real token of
+each document, cu_i + R_i. Without padding R_i = L_i; with padding-tolerant
+partitioning (see partition.pad_lengths) R_i is the real length and tokens at
+positions >= doc_end are pads.
 
 order[n_tiles]: tile indices sorted by n_kv descending, ties by index
 ascending (largest work first). Parity unpinned: it is a scheduling choice with
@@ -57,7 +62,7 @@ import numpy as np
 
 from . import partition
 
-VERSION = 2
+VERSION = 3
 TILE_FIELDS = ("q_local_start", "q_global_start", "n_rows", "doc", "slot",
                "kv_start", "n_kv_tiles", "n_full_kv_tiles")
 KVTILE_FIELDS = ("doc", "kv_global_start", "n_keys", "q_tile_begin", "q_tile_end",
@@ -85,6 +90,16 @@ def tiles(seqlens, cp: int, rank: int, block_t: int, block_n: int) -> np.ndarray
                 n_full = (q_glob - cu[i] + 1) // block_n
                 rows.append([cu[i] // cp + s * c + t0, q_glob, n_rows, i, s, cu[i], n_kv, n_full])
     return np.asarray(rows, dtype=np.int32).reshape(-1, 8)
+
+
+def doc_end(seqlens, cp: int, real_lengths=None) -> np.ndarray:
+    """One past the last real token of each document (padded layout)."""
+    lengths = partition.validate(seqlens, cp, 0)
+    cu = partition.cu_seqlens(lengths)
+    real = lengths if real_lengths is None else [int(x) for x in np.asarray(real_lengths).reshape(-1)]
+    if len(real) != len(lengths) or any(not 1 <= r <= length for r, length in zip(real, lengths)):
+        raise partition.PartitionError("real lengths must lie in [1, padded length]")
+    return np.asarray([cu[i] + real[i] for i in range(len(lengths))], dtype=np.int32)
 
 
 def order(tile_table: np.ndarray) -> np.ndarray:

@@ -46,6 +46,39 @@ def validate(seqlens, cp: int, rank: int) -> list[int]:
     return lengths
 
 
+def pad_lengths(real_lengths, cp: int) -> list[int]:
+    """Padded length of each document: the least multiple of 2*cp holding it.
+
+    Padding-tolerant partitioning (a reading: the subject page requires every
+    length to be divisible by 2*cp; this relaxes it). A document of R real
+    tokens is stored as L = ceil(R / 2cp) * 2cp tokens, its R real tokens
+    first and L - R pad tokens after them, and is partitioned like any other
+    document of length L. Every pad token comes after every real token of its
+    document, so the causal mask already hides the pads from real queries.
+    """
+    real = [int(x) for x in np.asarray(real_lengths).reshape(-1)]
+    if cp < 1:
+        raise PartitionError("cp must be >= 1")
+    if len(real) == 0:
+        raise PartitionError("at least one subsequence is required")
+    out = []
+    for r in real:
+        if r < 1:
+            raise PartitionError("subsequence lengths must be positive")
+        out.append(-(-r // (2 * cp)) * (2 * cp))
+    return out
+
+
+def pad_rows(real_lengths, cp: int, rank: int) -> np.ndarray:
+    """Bool per local row of the padded layout: True for pad tokens."""
+    lengths = pad_lengths(real_lengths, cp)
+    cu = cu_seqlens(lengths)
+    ends = [cu[i] + int(r) for i, r in enumerate(np.asarray(real_lengths).reshape(-1))]
+    docs = doc_of(lengths)
+    return np.asarray([g >= ends[int(docs[g])] for g in q_global(lengths, cp, rank).tolist()],
+                      dtype=bool)
+
+
 def cu_seqlens(lengths) -> list[int]:
     """Exclusive prefix sums: cu[0] = 0, cu[i+1] = cu[i] + L_i."""
     cu = [0]

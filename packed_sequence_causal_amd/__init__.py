@@ -27,8 +27,8 @@ STATUS_NAMES = {
     -5: "THD_EMISMATCH", -6: "THD_EHIP", -7: "THD_ENOMEM", -8: "THD_EUNSUPPORTED",
 }
 FIELDS = {"q_global": 0, "kv_row": 1, "chunk_off": 2, "tiles": 3, "order": 4, "kvtiles": 5,
-          "items": 6, "splits": 7}
-META_VERSION = 2
+          "items": 6, "splits": 7, "doc_end": 8}
+META_VERSION = 3
 
 
 class ThdError(RuntimeError):
@@ -46,6 +46,7 @@ class _Info(ctypes.Structure):
         ("n_tiles", ctypes.c_int64), ("n_kvtiles", ctypes.c_int64),
         ("useful_pairs", ctypes.c_int64), ("max_kv_tiles", ctypes.c_int64),
         ("n_items", ctypes.c_int64), ("n_splits", ctypes.c_int64), ("n_part_slots", ctypes.c_int64),
+        ("pad_tokens", ctypes.c_int64),
         ("concurrency", ctypes.c_int32), ("kv_split", ctypes.c_int32),
         ("n_docs", ctypes.c_int32), ("cp", ctypes.c_int32), ("rank", ctypes.c_int32),
         ("block_t", ctypes.c_int32), ("block_n", ctypes.c_int32), ("version", ctypes.c_int32),
@@ -67,6 +68,9 @@ def _load():
         "thd_plan_partition": (ctypes.c_int, [pi32, i32, i32, i32, pi64, pi64, pi32, pi32, pi32]),
         "thd_build_metadata": (ctypes.c_int, [pi32, i32, i32, i32, i32, i32, i32, i32,
                                               ctypes.POINTER(p)]),
+        "thd_pad_lengths": (ctypes.c_int, [pi32, i32, i32, pi32]),
+        "thd_build_metadata_padded": (ctypes.c_int, [pi32, i32, i32, i32, i32, i32, i32, i32,
+                                                     ctypes.POINTER(p)]),
         "thd_meta_info": (ctypes.c_int, [p, ctypes.POINTER(_Info)]),
         "thd_meta_copy": (ctypes.c_int, [p, i32, pi32, i64]),
         "thd_meta_release": (None, [p]),
@@ -88,7 +92,8 @@ def _load():
 
 
 _lib = _load()
-EXPORTS = ("thd_last_error", "thd_plan_partition", "thd_build_metadata", "thd_meta_info",
+EXPORTS = ("thd_last_error", "thd_plan_partition", "thd_build_metadata", "thd_pad_lengths",
+           "thd_build_metadata_padded", "thd_meta_info",
            "thd_meta_copy", "thd_meta_release", "thd_cache_stats", "thd_cache_clear",
            "thd_preferred_tiles", "thd_attn_fwd_workspace", "thd_attn_fwd",
            "thd_attn_bwd_workspace", "thd_attn_bwd")
@@ -147,7 +152,8 @@ class Meta:
         n = {"q_global": inf["local_tokens"], "kv_row": inf["total_tokens"],
              "chunk_off": inf["n_docs"] * 2 * inf["cp"], "tiles": inf["n_tiles"] * 8,
              "order": inf["n_tiles"], "kvtiles": inf["n_kvtiles"] * 8,
-             "items": inf["n_items"] * 4, "splits": inf["n_splits"] * 4}[name]
+             "items": inf["n_items"] * 4, "splits": inf["n_splits"] * 4,
+             "doc_end": inf["n_docs"]}[name]
         out = np.empty(n, np.int32)
         _check(_lib.thd_meta_copy(self._h, FIELDS[name], _ptr32(out), n))
         if name in ("tiles", "kvtiles"):
@@ -168,16 +174,27 @@ class Meta:
             pass
 
 
+def pad_lengths(*, seqlens, cp: int) -> np.ndarray:
+    """Padded length of each document: the least multiple of 2*cp holding it."""
+    lens = _lengths(seqlens)
+    out = np.empty_like(lens)
+    _check(_lib.thd_pad_lengths(_ptr32(lens), len(lens), cp, _ptr32(out)))
+    return out
+
+
 def build_metadata(*, seqlens, cp: int, rank: int, block_t: int, block_n: int,
-                   concurrency: int = 0, device: int = -1) -> Meta:
+                   concurrency: int = 0, device: int = -1, padded: bool = False) -> Meta:
     """Build or fetch cached metadata; device >= 0 also uploads it there.
 
     concurrency: work items of one kv head the device runs at once (0 = never
-    split a tile's key range)."""
+    split a tile's key range). padded: seqlens are real lengths of any size;
+    each document is stored padded to pad_lengths() tokens, real tokens first
+    (tensors use the padded layout; pad rows get O = 0 and LSE = +inf)."""
     lens = _lengths(seqlens)
     h = ctypes.c_void_p()
-    _check(_lib.thd_build_metadata(_ptr32(lens), len(lens), cp, rank, block_t, block_n,
-                                   concurrency, device, ctypes.byref(h)))
+    fn = _lib.thd_build_metadata_padded if padded else _lib.thd_build_metadata
+    _check(fn(_ptr32(lens), len(lens), cp, rank, block_t, block_n, concurrency, device,
+              ctypes.byref(h)))
     return Meta(h)
 
 
@@ -222,12 +239,12 @@ def device_concurrency(device: int, hkv: int) -> int:
 
 
 def device_metadata(*, seqlens, cp: int, rank: int, hq: int, hkv: int, d_qk: int, d_v: int,
-                    device: int, concurrency: int | None = None) -> Meta:
+                    device: int, concurrency: int | None = None, padded: bool = False) -> Meta:
     bt, bn = preferred_tiles(hq=hq, hkv=hkv, d_qk=d_qk, d_v=d_v)
     if concurrency is None:
         concurrency = device_concurrency(device, hkv)
     return build_metadata(seqlens=seqlens, cp=cp, rank=rank, block_t=bt, block_n=bn,
-                          concurrency=concurrency, device=device)
+                          concurrency=concurrency, device=device, padded=padded)
 
 
 def _workspace(device, nbytes: int):
@@ -242,13 +259,16 @@ def _workspace(device, nbytes: int):
 
 
 def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=None, lse=None,
-             out_f32=None, stream=None, meta: Meta | None = None, concurrency: int | None = None):
+             out_f32=None, stream=None, meta: Meta | None = None, concurrency: int | None = None,
+             padded: bool = False):
     """Forward attention for one rank. Returns (o bf16 [T_loc,Hq,dv], lse fp32 [T_loc,Hq]).
 
     q [T_loc, Hq, dqk], k [T, Hkv, dqk], v [T, Hkv, dv]: bf16 CUDA tensors,
     k/v already gathered rank-major. softmax_scale defaults to 1/sqrt(dqk).
     out_f32 (optional fp32 [T_loc, Hq, dv] tensor) also receives O in fp32,
     computed with split probabilities: pass it to attn_bwd as o_f32.
+    padded: seqlens are real lengths and the tensors use the padded layout
+    (see build_metadata); pad rows get O = 0 and LSE = +inf.
     """
     torch = _torch()
     hq, hkv, d_qk, d_v = q.shape[1], k.shape[1], q.shape[2], v.shape[2]
@@ -258,7 +278,7 @@ def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=No
     device = q.device.index
     if meta is None:
         meta = device_metadata(seqlens=seqlens, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=d_qk,
-                               d_v=d_v, device=device, concurrency=concurrency)
+                               d_v=d_v, device=device, concurrency=concurrency, padded=padded)
     inf = meta.info()
     if q.shape[0] != inf["local_tokens"] or k.shape[0] != inf["total_tokens"] \
             or v.shape[0] != inf["total_tokens"]:
@@ -284,17 +304,20 @@ def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=No
 
 
 def attn_bwd(*, q, k, v, lse, d_o, seqlens, cp: int, rank: int, softmax_scale=None,
-             o_f32=None, stream=None, meta: Meta | None = None, workspace=None):
+             o_f32=None, stream=None, meta: Meta | None = None, workspace=None,
+             padded: bool = False):
     """Backward for one rank. Returns (dq fp32, dk fp32, dv fp32); dk/dv are
     this rank's partial sums in the gathered layout (zeros for unseen keys).
     lse is the forward's. o_f32 (optional) is the forward's fp32 O from
-    attn_fwd(out_f32=...): D then comes from it instead of a pass over the keys."""
+    attn_fwd(out_f32=...): D then comes from it instead of a pass over the keys.
+    padded: as for attn_fwd; the forward's LSE = +inf on pad rows gives them
+    dQ = 0 and no share in dK, dV, whatever d_o holds there."""
     torch = _torch()
     hq, hkv, d_qk, d_v = q.shape[1], k.shape[1], q.shape[2], v.shape[2]
     device = q.device.index
     if meta is None:
         meta = device_metadata(seqlens=seqlens, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=d_qk,
-                               d_v=d_v, device=device)
+                               d_v=d_v, device=device, padded=padded)
     inf = meta.info()
     if q.shape[0] != inf["local_tokens"] or k.shape[0] != inf["total_tokens"]:
         raise ThdError(-5, "token counts do not match the lengths")

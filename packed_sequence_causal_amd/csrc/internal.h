@@ -22,10 +22,12 @@ struct Error {
 // Host-side plan and tile tables for one (lengths, cp, rank, block_t, block_n).
 // Field meanings are documented with THD_FIELD_* in thdattn.h.
 struct Plan {
-  std::vector<int32_t> seqlens;
+  std::vector<int32_t> seqlens;   // stored (padded) lengths
+  std::vector<int32_t> real;      // real lengths (equal to seqlens without padding)
   int32_t cp = 1, rank = 0, block_t = 1, block_n = 1, concurrency = 0, kv_split = 0;
   int64_t total = 0, local = 0, useful_pairs = 0, max_kv_tiles = 0, n_part_slots = 0;
-  std::vector<int32_t> q_global, kv_row, chunk_off, tiles, order, kvtiles, items, splits;
+  int64_t pad_tokens = 0;
+  std::vector<int32_t> q_global, kv_row, chunk_off, tiles, order, kvtiles, items, splits, doc_end;
 };
 
 // Checks lengths/cp/rank; throws Error. Returns T.
@@ -35,10 +37,11 @@ int64_t validate_partition(const int32_t* seqlens, int32_t n_docs, int32_t cp, i
 void plan_partition(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank,
                     int32_t* q_global, int32_t* kv_row, int32_t* chunk_off);
 
-// Builds the full plan (partition maps + tile tables).
+// Builds the full plan (partition maps + tile tables). real_lengths (may be
+// null: no padding) gives each document's real tokens, 1 <= R_i <= L_i.
 std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t cp,
                                  int32_t rank, int32_t block_t, int32_t block_n,
-                                 int32_t concurrency);
+                                 int32_t concurrency, const int32_t* real_lengths);
 
 // Device copies of the arrays the kernels read.
 struct DeviceMeta {
@@ -51,6 +54,7 @@ struct DeviceMeta {
   const int32_t* q_global = nullptr;
   const int32_t* items = nullptr;
   const int32_t* splits = nullptr;
+  const int32_t* doc_end = nullptr;
 };
 
 struct MetaEntry {
@@ -87,6 +91,7 @@ struct FwdParams {
   const int32_t* items;
   const int32_t* splits;
   const int32_t* kv_row;
+  const int32_t* doc_end;   // per document: one past its last real token
   int32_t n_items, n_splits, hq, hkv, group, block_t;
   int64_t total;
   float scale_log2;   // softmax_scale * log2(e)

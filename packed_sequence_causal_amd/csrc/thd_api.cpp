@@ -9,6 +9,7 @@
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 #include <cstring>
 #include <list>
@@ -63,18 +64,18 @@ struct DeviceScope {
 void upload(MetaEntry& e, int device) {
   const Plan& p = *e.plan;
   DeviceScope scope(device);
-  const std::vector<int32_t>* parts[7] = {&p.kv_row, &p.tiles, &p.order, &p.kvtiles,
-                                          &p.q_global, &p.items, &p.splits};
-  size_t offs[7];
+  const std::vector<int32_t>* parts[8] = {&p.kv_row, &p.tiles, &p.order, &p.kvtiles,
+                                          &p.q_global, &p.items, &p.splits, &p.doc_end};
+  size_t offs[8];
   size_t bytes = 0;
-  for (int i = 0; i < 7; ++i) {
+  for (int i = 0; i < 8; ++i) {
     offs[i] = bytes;
     bytes += (parts[i]->size() * sizeof(int32_t) + 255) / 256 * 256;
   }
   void* base = nullptr;
   check_hip(hipMalloc(&base, bytes == 0 ? 256 : bytes), "hipMalloc(metadata)");
   std::vector<char> staging(bytes);
-  for (int i = 0; i < 7; ++i)
+  for (int i = 0; i < 8; ++i)
     if (!parts[i]->empty())
       std::memcpy(staging.data() + offs[i], parts[i]->data(), parts[i]->size() * sizeof(int32_t));
   const hipError_t err = hipMemcpy(base, staging.data(), bytes, hipMemcpyHostToDevice);
@@ -92,6 +93,7 @@ void upload(MetaEntry& e, int device) {
   e.dev.q_global = reinterpret_cast<const int32_t*>(b + offs[4]);
   e.dev.items = reinterpret_cast<const int32_t*>(b + offs[5]);
   e.dev.splits = reinterpret_cast<const int32_t*>(b + offs[6]);
+  e.dev.doc_end = reinterpret_cast<const int32_t*>(b + offs[7]);
 }
 
 // Least-recently-used cache of metadata entries. Entries still referenced by a
@@ -111,12 +113,16 @@ Cache& cache() {
   return *c;
 }
 
-std::string make_key(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank,
-                     int32_t block_t, int32_t block_n, int32_t concurrency, int32_t device) {
-  const int32_t head[8] = {THD_META_VERSION, cp, rank, block_t, block_n, concurrency, device, n_docs};
-  std::string key(sizeof(head) + size_t(n_docs) * sizeof(int32_t), '\0');
+std::string make_key(const int32_t* seqlens, const int32_t* real, int32_t n_docs, int32_t cp,
+                     int32_t rank, int32_t block_t, int32_t block_n, int32_t concurrency,
+                     int32_t device) {
+  const int32_t head[9] = {THD_META_VERSION, cp,     rank,    block_t,          block_n,
+                           concurrency,      device, n_docs, real != nullptr ? 1 : 0};
+  const size_t n = size_t(n_docs) * sizeof(int32_t);
+  std::string key(sizeof(head) + (real != nullptr ? 2 : 1) * n, '\0');
   std::memcpy(&key[0], head, sizeof(head));
-  std::memcpy(&key[sizeof(head)], seqlens, size_t(n_docs) * sizeof(int32_t));
+  std::memcpy(&key[sizeof(head)], seqlens, n);
+  if (real != nullptr) std::memcpy(&key[sizeof(head) + n], real, n);
   return key;
 }
 
@@ -169,6 +175,67 @@ void check_kv_bytes(int64_t total, int32_t hkv, int32_t d_qk, int32_t d_v) {
   if (total * row >= (int64_t(1) << 32)) fail(THD_ERANGE, "K or V exceeds 4 GiB");
 }
 
+// L_i = ceil(R_i / 2cp) * 2cp (see thd_pad_lengths).
+void pad_lengths(const int32_t* real, int32_t n_docs, int32_t cp, int32_t* padded) {
+  if (real == nullptr || padded == nullptr) fail(THD_EINVAL, "a length array is NULL");
+  if (n_docs < 1) fail(THD_EINVAL, "n_docs must be >= 1");
+  if (cp < 1) fail(THD_ERANGE, "cp must be >= 1");
+  for (int32_t i = 0; i < n_docs; ++i) {
+    if (real[i] < 1) fail(THD_EINVAL, "document " + std::to_string(i) + " has length < 1");
+    const int64_t two = 2 * int64_t(cp);
+    const int64_t l = (int64_t(real[i]) + two - 1) / two * two;
+    if (l > INT32_MAX) fail(THD_ERANGE, "padded length beyond int32");
+    padded[i] = int32_t(l);
+  }
+}
+
+// Shared by thd_build_metadata (real = NULL) and thd_build_metadata_padded.
+void build_metadata_impl(const int32_t* seqlens, const int32_t* real, int32_t n_docs, int32_t cp,
+                         int32_t rank, int32_t block_t, int32_t block_n, int32_t concurrency,
+                         int32_t device, thd_meta** out) {
+  if (out == nullptr) fail(THD_EINVAL, "out is NULL");
+  *out = nullptr;
+  validate_partition(seqlens, n_docs, cp, rank);
+  if (device < -1) fail(THD_EINVAL, "device must be >= -1");
+  if (concurrency < 0) fail(THD_EINVAL, "concurrency must be >= 0");
+  if (device >= 0) {
+    int count = 0;
+    check_hip(hipGetDeviceCount(&count), "hipGetDeviceCount");
+    if (device >= count) fail(THD_EINVAL, "no such device " + std::to_string(device));
+  }
+  const std::string key =
+      make_key(seqlens, real, n_docs, cp, rank, block_t, block_n, concurrency, device);
+  Cache& c = cache();
+  std::lock_guard<std::mutex> lock(c.mu);
+  auto hit = c.map.find(key);
+  auto handle = std::make_unique<thd_meta>();
+  if (hit != c.map.end()) {
+    ++c.hits;
+    c.lru.splice(c.lru.begin(), c.lru, c.where[key]);
+    handle->entry = hit->second;
+    handle->cache_hit = true;
+  } else {
+    ++c.misses;
+    auto e = std::make_shared<MetaEntry>();
+    e->plan = build_plan(seqlens, n_docs, cp, rank, block_t, block_n, concurrency, real);
+    if (device >= 0) {
+      upload(*e, device);
+      ++c.uploads;
+    }
+    c.map.emplace(key, e);
+    c.lru.push_front(key);
+    c.where[key] = c.lru.begin();
+    while (c.map.size() > Cache::kCapacity) {
+      const std::string& victim = c.lru.back();
+      c.map.erase(victim);
+      c.where.erase(victim);
+      c.lru.pop_back();
+    }
+    handle->entry = std::move(e);
+  }
+  *out = handle.release();
+}
+
 }  // namespace
 
 MetaEntry::~MetaEntry() {
@@ -205,46 +272,26 @@ int thd_build_metadata(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32
                        int32_t block_t, int32_t block_n, int32_t concurrency, int32_t device,
                        thd_meta** out) {
   return guarded([&] {
+    build_metadata_impl(seqlens, nullptr, n_docs, cp, rank, block_t, block_n, concurrency, device,
+                        out);
+  });
+}
+
+int thd_pad_lengths(const int32_t* real_lengths, int32_t n_docs, int32_t cp, int32_t* padded) {
+  return guarded([&] { pad_lengths(real_lengths, n_docs, cp, padded); });
+}
+
+int thd_build_metadata_padded(const int32_t* real_lengths, int32_t n_docs, int32_t cp,
+                              int32_t rank, int32_t block_t, int32_t block_n,
+                              int32_t concurrency, int32_t device, thd_meta** out) {
+  return guarded([&] {
     if (out == nullptr) fail(THD_EINVAL, "out is NULL");
     *out = nullptr;
-    validate_partition(seqlens, n_docs, cp, rank);
-    if (device < -1) fail(THD_EINVAL, "device must be >= -1");
-    if (concurrency < 0) fail(THD_EINVAL, "concurrency must be >= 0");
-    if (device >= 0) {
-      int count = 0;
-      check_hip(hipGetDeviceCount(&count), "hipGetDeviceCount");
-      if (device >= count) fail(THD_EINVAL, "no such device " + std::to_string(device));
-    }
-    const std::string key = make_key(seqlens, n_docs, cp, rank, block_t, block_n, concurrency, device);
-    Cache& c = cache();
-    std::lock_guard<std::mutex> lock(c.mu);
-    auto hit = c.map.find(key);
-    auto handle = std::make_unique<thd_meta>();
-    if (hit != c.map.end()) {
-      ++c.hits;
-      c.lru.splice(c.lru.begin(), c.lru, c.where[key]);
-      handle->entry = hit->second;
-      handle->cache_hit = true;
-    } else {
-      ++c.misses;
-      auto e = std::make_shared<MetaEntry>();
-      e->plan = build_plan(seqlens, n_docs, cp, rank, block_t, block_n, concurrency);
-      if (device >= 0) {
-        upload(*e, device);
-        ++c.uploads;
-      }
-      c.map.emplace(key, e);
-      c.lru.push_front(key);
-      c.where[key] = c.lru.begin();
-      while (c.map.size() > Cache::kCapacity) {
-        const std::string& victim = c.lru.back();
-        c.map.erase(victim);
-        c.where.erase(victim);
-        c.lru.pop_back();
-      }
-      handle->entry = std::move(e);
-    }
-    *out = handle.release();
+    if (n_docs < 1) fail(THD_EINVAL, "n_docs must be >= 1");
+    std::vector<int32_t> padded(n_docs);
+    pad_lengths(real_lengths, n_docs, cp, padded.data());
+    build_metadata_impl(padded.data(), real_lengths, n_docs, cp, rank, block_t, block_n,
+                        concurrency, device, out);
   });
 }
 
@@ -262,6 +309,7 @@ int thd_meta_info(const thd_meta* meta, thd_meta_info_t* info) {
     info->n_items = int64_t(p.items.size() / 4);
     info->n_splits = int64_t(p.splits.size() / 4);
     info->n_part_slots = p.n_part_slots;
+    info->pad_tokens = p.pad_tokens;
     info->concurrency = p.concurrency;
     info->kv_split = p.kv_split;
     info->n_docs = int32_t(p.seqlens.size());
@@ -288,6 +336,7 @@ int thd_meta_copy(const thd_meta* meta, int32_t field, int32_t* dst, int64_t cou
       case THD_FIELD_KVTILES: src = &p.kvtiles; break;
       case THD_FIELD_ITEMS: src = &p.items; break;
       case THD_FIELD_SPLITS: src = &p.splits; break;
+      case THD_FIELD_DOC_END: src = &p.doc_end; break;
       default: fail(THD_EINVAL, "unknown field " + std::to_string(field));
     }
     if (count != int64_t(src->size()))
@@ -395,6 +444,7 @@ int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void*
     fp.items = d.items;
     fp.splits = d.splits;
     fp.kv_row = d.kv_row;
+    fp.doc_end = d.doc_end;
     fp.n_items = int32_t(n_items);
     fp.n_splits = int32_t(p.splits.size() / 4);
     fp.hq = hq;

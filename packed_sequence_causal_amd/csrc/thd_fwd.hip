@@ -163,6 +163,9 @@ __global__ __launch_bounds__(kFwdThreads, 2) void thd_fwd_kernel(FwdParams p) {
   const int n_rows = td[2];
   const int kv_start = td[5];
   const int n_full = td[7];
+  // Rows at or past the document's last real token are padding: written as
+  // O = 0, LSE = +inf (tokens are in position order within a tile).
+  const int n_real = min(max(p.doc_end[td[3]] - q_glob0, 0), n_rows);
   const int key_last = q_glob0 + n_rows - 1;   // keys past this are seen by no row
 
   // Row block rb of this wave holds rows 32 * (RB * wave + rb) + lane % 32.
@@ -449,6 +452,7 @@ __global__ __launch_bounds__(kFwdThreads, 2) void thd_fwd_kernel(FwdParams p) {
     }
     const size_t orow_idx = size_t(q_local0 + tok[rb]) * p.hq + head[rb];
     __bf16* orow = static_cast<__bf16*>(p.o) + orow_idx * DV;
+    const bool real = tok[rb] < n_real;   // pad rows get O = 0
 #pragma unroll
     for (int b = 0; b < S::DVB; ++b)
 #pragma unroll
@@ -457,14 +461,14 @@ __global__ __launch_bounds__(kFwdThreads, 2) void thd_fwd_kernel(FwdParams p) {
         bf16x4 out;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          o4[e] = acc[rb][b][4 * g + e] * inv;
+          o4[e] = real ? acc[rb][b][4 * g + e] * inv : 0.0f;
           out[e] = static_cast<__bf16>(o4[e]);
         }
         *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * g + 4 * half) = out;
         if constexpr (EXACT) *reinterpret_cast<f32x4*>(p.o_f32 + orow_idx * DV + 32 * b + 8 * g + 4 * half) = o4;
       }
     if (half == 0)
-      p.lse[size_t(q_local0 + tok[rb]) * p.hq + head[rb]] = (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2;
+      p.lse[orow_idx] = real ? (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : INFINITY;
   }
 }
 
@@ -491,6 +495,7 @@ __global__ __launch_bounds__(256) void thd_fwd_combine_kernel(FwdParams p) {
   const int32_t* td = p.tiles + size_t(tile) * 8;
   const int tok = row / G;
   if (tok >= td[2]) return;                  // row past the tile's last token
+  const bool pad = td[1] + tok >= p.doc_end[td[3]];   // written as O = 0, LSE = +inf
   const size_t slot_floats = size_t(fwd_partial_floats(p.block_t, G, DV));
   const float* base0 = p.partial + (size_t(first) * p.hkv + kvh) * slot_floats;
   const size_t part_stride = size_t(p.hkv) * slot_floats;
@@ -513,12 +518,12 @@ __global__ __launch_bounds__(256) void thd_fwd_combine_kernel(FwdParams p) {
   f32x4 o4;
 #pragma unroll
   for (int e = 0; e < 4; ++e) {
-    o4[e] = acc[e] * inv;
+    o4[e] = pad ? 0.0f : acc[e] * inv;
     out[e] = static_cast<__bf16>(o4[e]);
   }
   *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.o) + orow * DV + col) = out;
   if (p.o_f32 != nullptr) *reinterpret_cast<f32x4*>(p.o_f32 + orow * DV + col) = o4;
-  if (col == 0) p.lse[orow] = (mx + __builtin_amdgcn_logf(wsum)) * kLn2;
+  if (col == 0) p.lse[orow] = pad ? INFINITY : (mx + __builtin_amdgcn_logf(wsum)) * kLn2;
 }
 
 template <int DQK, int DV>

@@ -20,6 +20,8 @@
 #include <cstring>
 #include <numeric>
 
+#include <string>
+
 #include "internal.h"
 
 namespace thd {
@@ -72,14 +74,32 @@ void plan_partition(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t 
 
 std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t cp,
                                  int32_t rank, int32_t block_t, int32_t block_n,
-                                 int32_t concurrency) {
+                                 int32_t concurrency, const int32_t* real_lengths) {
   const int64_t total = validate_partition(seqlens, n_docs, cp, rank);
+  if (real_lengths != nullptr)
+    for (int32_t i = 0; i < n_docs; ++i)
+      if (real_lengths[i] < 1 || real_lengths[i] > seqlens[i])
+        fail(THD_EINVAL, "real length " + std::to_string(real_lengths[i]) + " of document " +
+                             std::to_string(i) + " is outside [1, " + std::to_string(seqlens[i]) + "]");
   if (block_t < 1 || block_n < 1 || block_t > 4096 || block_n > 4096)
     fail(THD_ERANGE, "tile sizes must be in [1, 4096]");
   if (concurrency < 0) fail(THD_EINVAL, "concurrency must be >= 0");
   auto plan = std::make_unique<Plan>();
   Plan& p = *plan;
   p.seqlens.assign(seqlens, seqlens + n_docs);
+  p.real.assign(real_lengths != nullptr ? real_lengths : seqlens,
+                (real_lengths != nullptr ? real_lengths : seqlens) + n_docs);
+  // One past each document's last real token (the padded layout puts a
+  // document's pad tokens after all of its real ones).
+  p.doc_end.resize(n_docs);
+  {
+    int64_t cu_d = 0;
+    for (int32_t i = 0; i < n_docs; ++i) {
+      p.doc_end[i] = int32_t(cu_d + p.real[i]);
+      p.pad_tokens += seqlens[i] - p.real[i];
+      cu_d += seqlens[i];
+    }
+  }
   p.cp = cp;
   p.rank = rank;
   p.block_t = block_t;

@@ -53,6 +53,8 @@ def _compare_plan(lengths, cp, rank, bt, bn, concurrency=0):
     assert info["useful_pairs"] == ometa.useful_pairs_closed_form(lengths, cp)
     assert info["max_kv_tiles"] == int(tt[:, 6].max())
     assert info["version"] == ometa.VERSION == thd.META_VERSION
+    assert np.array_equal(m.field("doc_end"), ometa.doc_end(lengths, cp))
+    assert info["pad_tokens"] == 0
     plan = thd.plan_partition(seqlens=lengths, cp=cp, rank=rank)
     assert np.array_equal(plan["q_global"], m.field("q_global"))
     assert np.array_equal(plan["kv_row"], m.field("kv_row"))
@@ -238,3 +240,47 @@ def test_concurrent_builds_agree():
     assert st["misses"] == len({(i, r) for i in range(4) for r in range(4)} & set(results))
     for (idx, rank), tiles in results.items():
         assert np.array_equal(tiles, ometa.tiles(cases[idx], 4, rank, 16, 64))
+
+
+# ---------------------------------------------------------------- padding
+
+@pytest.mark.parametrize("real,cp,rank", [
+    ([5, 13, 8], 2, 0), ([1, 3, 30], 4, 3), ([7, 9, 2], 3, 1), ([1], 8, 5),
+    ([100, 250, 31, 7, 64], 8, 2),
+])
+def test_padded_metadata_matches_the_oracle(real, cp, rank):
+    lengths = opart.pad_lengths(real, cp)
+    assert thd.pad_lengths(seqlens=real, cp=cp).tolist() == lengths
+    bt, bn = 16, 32
+    m = thd.build_metadata(seqlens=real, cp=cp, rank=rank, block_t=bt, block_n=bn, padded=True)
+    plain = thd.build_metadata(seqlens=lengths, cp=cp, rank=rank, block_t=bt, block_n=bn)
+    for name in ("q_global", "kv_row", "chunk_off", "tiles", "order", "kvtiles", "items", "splits"):
+        assert np.array_equal(m.field(name), plain.field(name)), name
+    assert np.array_equal(m.field("doc_end"), ometa.doc_end(lengths, cp, real))
+    assert np.array_equal(plain.field("doc_end"), ometa.doc_end(lengths, cp))
+    assert m.info()["pad_tokens"] == sum(lengths) - sum(real)
+    assert m.info()["total_tokens"] == sum(lengths)
+
+
+def test_padded_metadata_cache_key_holds_the_real_lengths():
+    a = thd.build_metadata(seqlens=[5, 8], cp=2, rank=0, block_t=8, block_n=16, padded=True)
+    b = thd.build_metadata(seqlens=[6, 8], cp=2, rank=0, block_t=8, block_n=16, padded=True)
+    c = thd.build_metadata(seqlens=[8, 8], cp=2, rank=0, block_t=8, block_n=16)
+    assert a.field("doc_end").tolist() == [5, 16]
+    assert b.field("doc_end").tolist() == [6, 16]
+    assert c.field("doc_end").tolist() == [8, 16]
+    again = thd.build_metadata(seqlens=[5, 8], cp=2, rank=0, block_t=8, block_n=16, padded=True)
+    assert again.info()["cache_hit"] == 1 and not b.info()["cache_hit"]
+
+
+@pytest.mark.parametrize("kwargs,status", [
+    ({"seqlens": [3, 0], "cp": 2}, "THD_EINVAL"),
+    ({"seqlens": [3], "cp": 0}, "THD_ERANGE"),
+    ({"seqlens": [2**31 - 1], "cp": 2}, "THD_ERANGE"),
+])
+def test_pad_lengths_errors(kwargs, status):
+    with pytest.raises(thd.ThdError) as e:
+        thd.pad_lengths(**kwargs)
+    assert e.value.status == status
+    with pytest.raises(thd.ThdError):
+        thd.build_metadata(block_t=8, block_n=16, rank=0, padded=True, **kwargs)

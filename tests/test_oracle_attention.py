@@ -237,3 +237,103 @@ def test_workload_shapes_tiny_runs():
     o, lse = attention.attn_fwd64_rows(q, b.k.double().numpy(), b.v.double().numpy(),
                                        b.lengths, w.cp, w.rank, rows)
     assert np.all(np.isfinite(o)) and np.all(np.isfinite(lse))
+
+
+# ---------------------------------------------------------------- padding
+# Pins of the padded layout (documents of any length, padded at their end to
+# a multiple of 2*cp): real rows against PyTorch on the unpadded sequence of
+# real tokens alone, which knows nothing of the partition or the pads.
+
+def _padded_case(seed, real, cp, hq, hkv, dqk, dv):
+    rng = np.random.default_rng(seed)
+    total = int(sum(partition.pad_lengths(real, cp)))
+    q = rng.standard_normal((total // cp, hq, dqk))
+    k = rng.standard_normal((total, hkv, dqk))
+    v = rng.standard_normal((total, hkv, dv))
+    do = rng.standard_normal((total // cp, hq, dv))
+    return q, k, v, do
+
+
+def _real_sequence(real, cp):
+    """Padded global position of every real token, in order; document of each."""
+    lengths = partition.pad_lengths(real, cp)
+    cu = partition.cu_seqlens(lengths)
+    pos, doc = [], []
+    for i, r in enumerate(real):
+        pos.extend(range(cu[i], cu[i] + r))
+        doc.extend([i] * r)
+    return np.asarray(pos), np.asarray(doc)
+
+
+def _unpadded_library(q_loc, k, v, do, real, cp, rank, scale):
+    """O, LSE and gradients from float64 PyTorch on the real tokens only."""
+    lengths = partition.pad_lengths(real, cp)
+    pos, doc = _real_sequence(real, cp)
+    n = pos.shape[0]
+    qg = partition.q_global(lengths, cp, rank)
+    rows = partition.kv_row(lengths, cp)
+    where = {int(g): j for j, g in enumerate(pos.tolist())}
+    local_real = [l for l, g in enumerate(qg.tolist()) if int(g) in where]
+    real_idx = [where[int(qg[l])] for l in local_real]
+    group = q_loc.shape[1] // k.shape[1]
+    q_full = np.random.default_rng(5).standard_normal((n,) + q_loc.shape[1:])
+    q_full[real_idx] = q_loc[local_real]
+    idx = np.arange(n)
+    mask = (doc[:, None] == doc[None, :]) & (idx[None, :] <= idx[:, None])
+    qt = torch.from_numpy(q_full).requires_grad_()
+    kt = torch.from_numpy(k[rows[pos]]).requires_grad_()
+    vt = torch.from_numpy(v[rows[pos]]).requires_grad_()
+    s = scale * torch.einsum("ihd,jhd->hij", qt, kt.repeat_interleave(group, dim=1))
+    s = s.masked_fill(~torch.from_numpy(mask)[None], -math.inf)
+    lse = torch.logsumexp(s, dim=2)                           # [h, n]
+    out = torch.einsum("hij,jhd->ihd", torch.exp(s - lse[:, :, None]),
+                       vt.repeat_interleave(group, dim=1))
+    sel = torch.from_numpy(np.asarray(real_idx, dtype=np.int64))
+    (out[sel] * torch.from_numpy(do[local_real])).sum().backward()
+    dq = np.zeros_like(q_loc)
+    dq[local_real] = qt.grad.numpy()[real_idx]
+    dk = np.zeros_like(k)
+    dvv = np.zeros_like(v)
+    dk[rows[pos]] = kt.grad.numpy()
+    dvv[rows[pos]] = vt.grad.numpy()
+    o = np.zeros((q_loc.shape[0], q_loc.shape[1], v.shape[2]))
+    o[local_real] = out.detach().numpy()[real_idx]
+    lse_loc = np.full(q_loc.shape[:2], np.inf)
+    lse_loc[local_real] = lse.detach().numpy().T[real_idx]
+    return o, lse_loc, dq, dk, dvv
+
+
+@pytest.mark.parametrize("real,cp,rank,hq,hkv,dqk,dv", [
+    ([5, 13, 8], 2, 0, 2, 1, 8, 4),      # pads inside the last chunk
+    ([1, 3, 30], 4, 3, 4, 2, 6, 6),      # a 1-token document: pads span 7 chunks
+    ([7, 9, 2], 3, 1, 3, 3, 5, 7),
+    ([16, 4], 2, 1, 2, 2, 4, 4),         # one document needs no pad
+])
+def test_padded_layout_matches_unpadded_library(real, cp, rank, hq, hkv, dqk, dv):
+    q, k, v, do = _padded_case(31, real, cp, hq, hkv, dqk, dv)
+    scale = 0.37
+    o, lse = attention.attn_fwd64_padded(q, k, v, real, cp, rank, scale=scale)
+    dq, dk, dvv = attention.attn_bwd64_padded(q, k, v, do, real, cp, rank, scale=scale)
+    ro, rlse, rdq, rdk, rdv = _unpadded_library(q, k, v, do, real, cp, rank, scale)
+    pad = partition.pad_rows(real, cp, rank)
+    assert np.max(np.abs(o - ro)) <= 1e-12
+    assert np.all(np.isinf(lse[pad])) and np.all(lse[pad] > 0)
+    assert np.max(np.abs(lse[~pad] - rlse[~pad])) <= 1e-12
+    assert np.all(o[pad] == 0.0) and np.all(dq[pad] == 0.0)
+    for a, b in ((dq, rdq), (dk, rdk), (dvv, rdv)):
+        assert np.max(np.abs(a - b)) <= 1e-11
+    # pad keys get exact zeros, whatever dO holds on pad rows
+    lengths = partition.pad_lengths(real, cp)
+    pos, _ = _real_sequence(real, cp)
+    is_real = np.zeros(sum(lengths), dtype=bool)
+    is_real[pos] = True
+    pad_keys = partition.kv_row(lengths, cp)[~is_real]
+    assert np.all(dk[pad_keys] == 0.0) and np.all(dvv[pad_keys] == 0.0)
+
+
+def test_padding_without_pads_is_the_plain_oracle():
+    real, cp, rank = [8, 16, 8], 2, 1
+    q, k, v, do = _padded_case(32, real, cp, 4, 2, 8, 8)
+    o, lse = attention.attn_fwd64_padded(q, k, v, real, cp, rank)
+    o2, lse2 = attention.attn_fwd64(q, k, v, real, cp, rank)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)

@@ -193,3 +193,33 @@ def test_work_items_cover_each_tile_once(concurrency):
                 # every part starts with a KV tile all rows see whole
                 assert all(m[0] <= tt[t, 7] - 1 for m in mine)
             assert sorted(slots) == list(range(len(slots)))
+
+
+def test_pad_lengths_closed_form():
+    rng = np.random.default_rng(3)
+    for cp in (1, 2, 3, 8):
+        real = rng.integers(1, 200, size=40).tolist()
+        padded = partition.pad_lengths(real, cp)
+        for r, length in zip(real, padded):
+            assert length % (2 * cp) == 0 and r <= length < r + 2 * cp
+    assert partition.pad_lengths([1, 4, 5], 2) == [4, 4, 8]
+    with pytest.raises(partition.PartitionError):
+        partition.pad_lengths([3, 0], 2)
+
+
+def test_pad_rows_are_the_tokens_past_each_real_end():
+    real, cp = [1, 5, 8, 21], 2
+    lengths = partition.pad_lengths(real, cp)
+    cu = partition.cu_seqlens(lengths)
+    total_pads = 0
+    for rank in range(cp):
+        pad = partition.pad_rows(real, cp, rank)
+        qg = partition.q_global(lengths, cp, rank)
+        docs = partition.doc_of(lengths)
+        for l, g in enumerate(qg.tolist()):
+            assert pad[l] == (g >= cu[int(docs[g])] + real[int(docs[g])])
+        total_pads += int(pad.sum())
+    assert total_pads == sum(lengths) - sum(real)
+    ends = metadata.doc_end(lengths, cp, real)
+    assert ends.tolist() == [cu[i] + real[i] for i in range(len(real))]
+    assert metadata.doc_end(lengths, cp).tolist() == cu[1:]
