@@ -104,7 +104,13 @@ def _check(code: int):
         raise ThdError(code, _lib.thd_last_error().decode(errors="replace"))
 
 
+_I32 = np.dtype(np.int32)
+
+
 def _lengths(seqlens) -> np.ndarray:
+    if type(seqlens) is np.ndarray and seqlens.dtype == _I32 and seqlens.ndim == 1 \
+            and seqlens.flags.c_contiguous:
+        return seqlens   # already what the library takes: no copy, no range check needed
     arr = np.ascontiguousarray(np.asarray(seqlens).reshape(-1))
     if arr.size and not np.issubdtype(arr.dtype, np.integer):
         raise TypeError("seqlens must be integers")
@@ -137,15 +143,32 @@ class Meta:
 
     def __init__(self, handle):
         self._h = handle
+        self._info = None   # a handle's info never changes: read it once
+        self._fwd_ws = {}   # forward workspace bytes per (hq, hkv, d_v)
 
     @property
     def handle(self):
         return self._h
 
     def info(self) -> dict:
-        inf = _Info()
-        _check(_lib.thd_meta_info(self._h, ctypes.byref(inf)))
-        return {name: getattr(inf, name) for name, _ in _Info._fields_}
+        if self._info is None:
+            inf = _Info()
+            _check(_lib.thd_meta_info(self._h, ctypes.byref(inf)))
+            self._info = {name: getattr(inf, name) for name, _ in _Info._fields_}
+        return dict(self._info)
+
+    def _cached_info(self) -> dict:
+        if self._info is None:
+            self.info()
+        return self._info
+
+    def fwd_workspace_bytes(self, hq: int, hkv: int, d_v: int) -> int:
+        key = (hq, hkv, d_v)
+        if key not in self._fwd_ws:
+            need = ctypes.c_int64()
+            _check(_lib.thd_attn_fwd_workspace(self._h, hq, hkv, d_v, ctypes.byref(need)))
+            self._fwd_ws[key] = need.value
+        return self._fwd_ws[key]
 
     def field(self, name: str) -> np.ndarray:
         inf = self.info()
@@ -198,10 +221,16 @@ def build_metadata(*, seqlens, cp: int, rank: int, block_t: int, block_n: int,
     return Meta(h)
 
 
+_TILES = {}
+
+
 def preferred_tiles(*, hq: int, hkv: int, d_qk: int, d_v: int) -> tuple[int, int]:
-    bt, bn = ctypes.c_int32(), ctypes.c_int32()
-    _check(_lib.thd_preferred_tiles(hq, hkv, d_qk, d_v, ctypes.byref(bt), ctypes.byref(bn)))
-    return bt.value, bn.value
+    key = (hq, hkv, d_qk, d_v)
+    if key not in _TILES:
+        bt, bn = ctypes.c_int32(), ctypes.c_int32()
+        _check(_lib.thd_preferred_tiles(hq, hkv, d_qk, d_v, ctypes.byref(bt), ctypes.byref(bn)))
+        _TILES[key] = (bt.value, bn.value)
+    return _TILES[key]
 
 
 def cache_stats() -> dict:
@@ -279,13 +308,12 @@ def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=No
     if meta is None:
         meta = device_metadata(seqlens=seqlens, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=d_qk,
                                d_v=d_v, device=device, concurrency=concurrency, padded=padded)
-    inf = meta.info()
+    inf = meta._cached_info()
     if q.shape[0] != inf["local_tokens"] or k.shape[0] != inf["total_tokens"] \
             or v.shape[0] != inf["total_tokens"]:
         raise ThdError(-5, "token counts do not match the lengths")
-    need = ctypes.c_int64()
-    _check(_lib.thd_attn_fwd_workspace(meta.handle, hq, hkv, d_v, ctypes.byref(need)))
-    ws = _workspace(q.device, need.value)
+    need = meta.fwd_workspace_bytes(hq, hkv, d_v)
+    ws = _workspace(q.device, need)
     if out is None:
         out = torch.empty((q.shape[0], hq, d_v), dtype=torch.bfloat16, device=q.device)
     if lse is None:
@@ -298,7 +326,7 @@ def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=No
                              out.data_ptr(), lse.data_ptr(),
                              None if out_f32 is None else out_f32.data_ptr(),
                              hq, hkv, d_qk, d_v, scale,
-                             None if ws is None else ws.data_ptr(), need.value,
+                             None if ws is None else ws.data_ptr(), need,
                              _stream_handle(stream, q.device)))
     return out, lse
 
@@ -318,7 +346,7 @@ def attn_bwd(*, q, k, v, lse, d_o, seqlens, cp: int, rank: int, softmax_scale=No
     if meta is None:
         meta = device_metadata(seqlens=seqlens, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=d_qk,
                                d_v=d_v, device=device, padded=padded)
-    inf = meta.info()
+    inf = meta._cached_info()
     if q.shape[0] != inf["local_tokens"] or k.shape[0] != inf["total_tokens"]:
         raise ThdError(-5, "token counts do not match the lengths")
     need = ctypes.c_int64()

@@ -26,15 +26,15 @@
 //   dS (and P in dV = P^T dO) enter their products as a pair of bf16 values
 //   (hi, lo = x - hi), so their rounding error is ~2^-17 instead of bf16's
 //   2^-9: the gradients are then limited by fp32 accumulation only;
-//   thd_bwd_dkdv_kernel: one workgroup (2 waves, 32 keys each) per
+//   thd_bwd_dkdv_kernel: one workgroup (4 waves, 16 keys each) per
 //      (64-key tile, kv head). The key tiles cover every key once; the query
 //      tiles that see a key tile are a suffix of its document's tiles, walked
 //      in 32-row blocks (token-major rows: all G heads of a kv head) through a
-//      two-stage LDS ring. S = Q K^T and dP = dO V^T leave each lane with one
-//      key and 16 rows, which is the A-operand layout of P^T and dS^T, so
-//      dV += P^T dO and dK += dS^T Q take their B operands from the row-major
-//      dO and Q blocks with transpose reads. Tiles no local query sees write
-//      zeros.
+//      three-stage LDS ring. S = Q K^T and dP = dO V^T on 16x16x32 MFMA leave
+//      each lane with one key and 8 rows, which is the A-operand layout of P^T
+//      and dS^T, so dV += P^T dO and dK += dS^T Q take their B operands from
+//      the row-major dO and Q blocks with transpose reads. Tiles no local
+//      query sees write zeros.
 #include <hip/hip_runtime.h>
 
 #include <climits>
