@@ -256,7 +256,6 @@ def _stream_handle(stream, device):
 
 
 _CUS = {}
-_WORKSPACE = {}
 FWD_WORKGROUPS_PER_CU = 2   # the forward kernel's occupancy (LDS and registers)
 
 
@@ -276,14 +275,17 @@ def device_metadata(*, seqlens, cp: int, rank: int, hq: int, hkv: int, d_qk: int
                           concurrency=concurrency, device=device, padded=padded)
 
 
-def _workspace(device, nbytes: int):
-    """A cached device buffer of at least nbytes (None for 0)."""
+def _scratch(device, nbytes: int, stream):
+    """A device buffer of nbytes (None for 0) from torch's caching allocator,
+    fresh per call: calls on different streams never share it. When the kernel
+    runs on a stream other than the current one, the buffer is recorded on it,
+    so the allocator does not hand it out again before that stream's work ends."""
     if nbytes <= 0:
         return None
-    buf = _WORKSPACE.get(device)
-    if buf is None or buf.numel() < nbytes:
-        buf = _torch().empty(nbytes, dtype=_torch().uint8, device=device)
-        _WORKSPACE[device] = buf
+    torch = _torch()
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if stream is not None and stream != torch.cuda.current_stream(device):
+        buf.record_stream(stream)
     return buf
 
 
@@ -313,7 +315,7 @@ def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=No
             or v.shape[0] != inf["total_tokens"]:
         raise ThdError(-5, "token counts do not match the lengths")
     need = meta.fwd_workspace_bytes(hq, hkv, d_v)
-    ws = _workspace(q.device, need)
+    ws = _scratch(q.device, need, stream)
     if out is None:
         out = torch.empty((q.shape[0], hq, d_v), dtype=torch.bfloat16, device=q.device)
     if lse is None:
@@ -352,7 +354,7 @@ def attn_bwd(*, q, k, v, lse, d_o, seqlens, cp: int, rank: int, softmax_scale=No
     need = ctypes.c_int64()
     _check(_lib.thd_attn_bwd_workspace(meta.handle, hq, ctypes.byref(need)))
     if workspace is None:
-        workspace = torch.empty(need.value, dtype=torch.uint8, device=q.device)
+        workspace = _scratch(q.device, need.value, stream)
     dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
     dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
     dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)

@@ -94,6 +94,38 @@ def test_forward_split_key_ranges_match_oracle(case, concurrency):
     assert (lse - lse1).abs().max().item() <= 1e-4
 
 
+def test_split_forward_and_backward_on_side_streams():
+    """Calls on two side streams at once (split forward, whose partial results
+    need a workspace, then the backward) give bit-identical results to the same
+    calls on the current stream: per-call workspaces are never shared."""
+    seed, lengths, cp, rank, hq, hkv, dqk, dv = SPLIT[0]
+    b = workloads.small_case(seed, lengths, cp, hq, hkv, dqk, dv, backward=True, rank=rank)
+    dev = device()
+    q, k, v, do = (t.to(dev) for t in (b.q, b.k, b.v, b.do))
+    meta = thd.device_metadata(seqlens=b.lengths, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=dqk,
+                               d_v=dv, device=0, concurrency=64)
+    assert meta.info()["n_splits"] > 0
+    print(f"[fwd streams] seed={seed}", flush=True)
+
+    def run(stream):
+        o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=b.lengths, cp=cp, rank=rank, meta=meta,
+                              stream=stream)
+        g = thd.attn_bwd(q=q, k=k, v=v, lse=lse, d_o=do, seqlens=b.lengths, cp=cp, rank=rank,
+                         meta=meta, stream=stream)
+        return (o, lse) + g
+
+    want = run(None)
+    torch.cuda.synchronize()
+    side = [torch.cuda.Stream(device=dev) for _ in range(2)]
+    for s in side:
+        s.wait_stream(torch.cuda.current_stream(dev))
+    got = [run(s) for s in side]
+    torch.cuda.synchronize()
+    for res in got:
+        for name, a, w in zip(("O", "LSE", "dQ", "dK", "dV"), res, want):
+            assert torch.equal(a, w), name
+
+
 EXACT = [
     # (seed, lengths, cp, rank, hq, hkv, dqk, dv, concurrency)
     (81, [256, 512, 256], 2, 0, 8, 8, 64, 64, 0),
