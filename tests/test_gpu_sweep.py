@@ -3,7 +3,7 @@
 The other GPU tests cover the workloads' shapes; this grid covers the rest of
 the supported space: group sizes from 1 to the maximum 128 (a query tile of a
 single token), groups that do not divide 128 or the 32-row backward blocks,
-context-parallel sizes 1 to 8 with first, middle and last ranks, documents of
+context-parallel sizes 1 to 16 with first, middle and last ranks, documents of
 the minimum length 2*cp (one row per chunk) beside long ones, and every
 supported head-dimension pair. Each case runs the forward (bf16 P, and split
 probabilities with the fp32 O), the forward with the finest split of long key
@@ -32,6 +32,7 @@ GRID = [
     (97, [6, 6, 6, 6, 6, 600], 3, 0, 24, 4, 128, 128),       # group 6, one-row chunks
     (98, [2, 2, 1022], 1, 0, 4, 4, 192, 128),                # cp 1, group 1
     (99, [16] * 10 + [512], 8, 7, 64, 8, 128, 128),          # cp 8, last rank, minimal documents
+    (100, [32, 96, 640], 16, 9, 16, 4, 128, 128),            # cp 16: chunks of 1 to 20 tokens
 ]
 
 

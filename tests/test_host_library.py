@@ -81,6 +81,17 @@ def test_metadata_bit_exact_random(seed):
     _compare_plan(lengths, cp, int(rng.integers(0, cp)), bt, bn, int(rng.choice([0, 1, 4, 50])))
 
 
+@pytest.mark.parametrize("seed", range(4))
+def test_metadata_bit_exact_large_cp(seed):
+    """Context-parallel sizes beyond the workloads' (16 to 64), where a document's chunks
+    are a few tokens long and most tiles hold a single chunk."""
+    rng = np.random.default_rng(2000 + seed)
+    cp = int(rng.choice([16, 32, 64]))
+    lengths = workloads.random_lengths(rng, int(rng.integers(1, 6)), cp, 12)
+    bt = int(rng.choice([1, 4, 16, 32]))
+    _compare_plan(lengths, cp, int(rng.integers(0, cp)), bt, 64, int(rng.choice([0, 4, 50])))
+
+
 def test_preferred_tiles():
     assert thd.preferred_tiles(hq=32, hkv=8, d_qk=128, d_v=128) == (32, 64)
     assert thd.preferred_tiles(hq=64, hkv=8, d_qk=128, d_v=128) == (16, 64)
