@@ -144,13 +144,17 @@ def main(argv=None) -> int:
            if w.backward else None)
 
     def step():
+        # The forward's tile sizes depend on the batch (32-key tiles for short
+        # documents); the backward's are fixed per head shape.
         meta = thd.device_metadata(seqlens=batch.lengths, cp=w.cp, rank=w.rank, hq=w.hq,
-                                   hkv=w.hkv, d_qk=w.d_qk, d_v=w.d_v, device=0)
+                                   hkv=w.hkv, d_qk=w.d_qk, d_v=w.d_v, device=0, forward=True)
         thd.attn_fwd(q=q, k=k, v=v, seqlens=batch.lengths, cp=w.cp, rank=w.rank, out=o, lse=lse,
                      out_f32=o32, meta=meta)
         if w.backward:
+            meta_b = thd.device_metadata(seqlens=batch.lengths, cp=w.cp, rank=w.rank, hq=w.hq,
+                                         hkv=w.hkv, d_qk=w.d_qk, d_v=w.d_v, device=0)
             thd.attn_bwd(q=q, k=k, v=v, lse=lse, d_o=do, seqlens=batch.lengths, cp=w.cp,
-                         rank=w.rank, o_f32=o32, meta=meta)
+                         rank=w.rank, o_f32=o32, meta=meta_b)
 
     # Parity gate: no throughput is reported for a path that disagrees with the oracle.
     step()
@@ -181,7 +185,7 @@ def main(argv=None) -> int:
     # Forward kernel duration: HIP events around each launch on the launch stream.
     stream = torch.cuda.current_stream(dev)
     meta = thd.device_metadata(seqlens=batch.lengths, cp=w.cp, rank=w.rank, hq=w.hq, hkv=w.hkv,
-                               d_qk=w.d_qk, d_v=w.d_v, device=0)
+                               d_qk=w.d_qk, d_v=w.d_v, device=0, forward=True)
     n_ev = max(10, min(args.steps, 100))
     starts = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
     ends = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
@@ -215,7 +219,7 @@ def main(argv=None) -> int:
     per_rank = []
     for r in range(w.cp):
         meta_r = thd.device_metadata(seqlens=batch.lengths, cp=w.cp, rank=r, hq=w.hq, hkv=w.hkv,
-                                     d_qk=w.d_qk, d_v=w.d_v, device=0)
+                                     d_qk=w.d_qk, d_v=w.d_v, device=0, forward=True)
         for _ in range(3):
             thd.attn_fwd(q=q, k=k, v=v, seqlens=batch.lengths, cp=w.cp, rank=r, out=o, lse=lse,
                          meta=meta_r, stream=stream)
@@ -266,7 +270,9 @@ def main(argv=None) -> int:
         "config": {"workload": w.name, "T": w.total, "cp": w.cp, "rank": w.rank, "hq": w.hq,
                    "hkv": w.hkv, "d_qk": w.d_qk, "d_v": w.d_v, "n_docs": int(len(batch.lengths)),
                    "lengths_sha16": workloads.lengths_digest(batch.lengths),
-                   "useful_pairs": int(pairs), "backward": bool(w.backward)},
+                   "useful_pairs": int(pairs), "backward": bool(w.backward),
+                   "fwd_block_t": int(meta.info()["block_t"]),
+                   "fwd_block_n": int(meta.info()["block_n"])},
         "pct_of_bf16_peak": round(100.0 * value / PEAK_BF16_TFLOPS, 2),
         "roofline": roof,
         "timing": {"fwd_kernel_ms_median_warm": round(float(np.median(warm)), 5),

@@ -186,9 +186,29 @@ int thd_cache_stats(int64_t* hits, int64_t* misses, int64_t* uploads, int64_t* e
 int thd_cache_clear(void);
 
 /* Tile sizes the kernels expect for a head shape: block_t query tokens per
- * tile and block_n keys per KV tile. THD_EUNSUPPORTED if no kernel exists. */
+ * tile and block_n keys per KV tile. THD_EUNSUPPORTED if no kernel exists.
+ * These sizes serve the forward and the backward alike. */
 int thd_preferred_tiles(int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
                         int32_t* block_t, int32_t* block_n);
+
+/* Tile sizes for the forward of one batch (seqlens[n_docs] as laid out, i.e.
+ * padded lengths for the padded layout; host). The forward also has 32-key
+ * tile kernels for d_qk <= 128, run three workgroups per CU instead of two:
+ * chosen (block_n = 32) when no query tile of this rank sees more than 512
+ * keys, i.e. (2cp - rank) * L_i / (2cp) <= 512 for every document, else
+ * block_n = 64. block_t as thd_preferred_tiles. Metadata built with block_n =
+ * 32 serves thd_attn_fwd only: thd_attn_bwd needs block_n = 64 (THD_EMISMATCH
+ * otherwise). Errors as thd_plan_partition, plus THD_EUNSUPPORTED. */
+int thd_preferred_fwd_tiles(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank,
+                            int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v, int32_t* block_t,
+                            int32_t* block_n);
+
+/* Forward work items of one kv head that a device runs at once: its CUs times
+ * the forward workgroups per CU for this KV tile size (2 for block_n = 64, 3
+ * for 32), over hkv (at least 1). Pass it as thd_build_metadata's
+ * concurrency. Errors: THD_EINVAL (hkv < 1, block_n not 32 or 64, NULL
+ * output, no such device), THD_EHIP. */
+int thd_fwd_concurrency(int32_t device, int32_t hkv, int32_t block_n, int32_t* concurrency);
 
 /* Bytes of device workspace thd_attn_fwd needs for the partial results of
  * split tiles (0 when no tile is split). */
@@ -197,7 +217,7 @@ int thd_attn_fwd_workspace(const thd_meta* meta, int32_t hq, int32_t hkv, int32_
 
 /* Forward: o and lse for every local query row and q head.
  * meta must come from thd_build_metadata with the tile sizes of
- * thd_preferred_tiles and the current device. softmax_scale > 0 (callers
+ * thd_preferred_tiles or thd_preferred_fwd_tiles and the current device. softmax_scale > 0 (callers
  * usually pass 1/sqrt(d_qk)). Supported (d_qk, d_v): (64,64), (128,128),
  * (192,128); Hq/Hkv <= 128. q, k, v, o, lse must be 16-byte aligned; k and v
  * must each be smaller than 4 GiB (THD_ERANGE otherwise). workspace (16-byte

@@ -77,6 +77,9 @@ def _load():
         "thd_cache_stats": (ctypes.c_int, [pi64, pi64, pi64, pi64]),
         "thd_cache_clear": (ctypes.c_int, []),
         "thd_preferred_tiles": (ctypes.c_int, [i32, i32, i32, i32, pi32, pi32]),
+        "thd_preferred_fwd_tiles": (ctypes.c_int, [pi32, i32, i32, i32, i32, i32, i32, i32, pi32,
+                                                   pi32]),
+        "thd_fwd_concurrency": (ctypes.c_int, [i32, i32, i32, pi32]),
         "thd_attn_fwd_workspace": (ctypes.c_int, [p, i32, i32, i32, pi64]),
         "thd_attn_fwd": (ctypes.c_int, [p, p, p, p, p, p, p, i32, i32, i32, i32, ctypes.c_float, p,
                                         i64, p]),
@@ -95,7 +98,8 @@ _lib = _load()
 EXPORTS = ("thd_last_error", "thd_plan_partition", "thd_build_metadata", "thd_pad_lengths",
            "thd_build_metadata_padded", "thd_meta_info",
            "thd_meta_copy", "thd_meta_release", "thd_cache_stats", "thd_cache_clear",
-           "thd_preferred_tiles", "thd_attn_fwd_workspace", "thd_attn_fwd",
+           "thd_preferred_tiles", "thd_preferred_fwd_tiles", "thd_fwd_concurrency",
+           "thd_attn_fwd_workspace", "thd_attn_fwd",
            "thd_attn_bwd_workspace", "thd_attn_bwd")
 
 
@@ -255,22 +259,43 @@ def _stream_handle(stream, device):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-_CUS = {}
-FWD_WORKGROUPS_PER_CU = 2   # the forward kernel's occupancy (LDS and registers)
+_CONCURRENCY = {}
 
 
-def device_concurrency(device: int, hkv: int) -> int:
-    """Forward work items of one kv head the device runs at once."""
-    if device not in _CUS:
-        _CUS[device] = _torch().cuda.get_device_properties(device).multi_processor_count
-    return max(1, _CUS[device] * FWD_WORKGROUPS_PER_CU // hkv)
+def preferred_fwd_tiles(*, seqlens, cp: int, rank: int, hq: int, hkv: int, d_qk: int, d_v: int,
+                        padded: bool = False) -> tuple[int, int]:
+    """Forward tile sizes for this batch (thd_preferred_fwd_tiles): 32-key
+    tiles when no query tile sees more than 512 keys and d_qk <= 128."""
+    lens = pad_lengths(seqlens=seqlens, cp=cp) if padded else _lengths(seqlens)
+    bt, bn = ctypes.c_int32(), ctypes.c_int32()
+    _check(_lib.thd_preferred_fwd_tiles(_ptr32(lens), len(lens), cp, rank, hq, hkv, d_qk, d_v,
+                                        ctypes.byref(bt), ctypes.byref(bn)))
+    return bt.value, bn.value
+
+
+def device_concurrency(device: int, hkv: int, block_n: int = 64) -> int:
+    """Forward work items of one kv head the device runs at once (thd_fwd_concurrency)."""
+    key = (device, hkv, block_n)
+    if key not in _CONCURRENCY:
+        c = ctypes.c_int32()
+        _check(_lib.thd_fwd_concurrency(device, hkv, block_n, ctypes.byref(c)))
+        _CONCURRENCY[key] = c.value
+    return _CONCURRENCY[key]
 
 
 def device_metadata(*, seqlens, cp: int, rank: int, hq: int, hkv: int, d_qk: int, d_v: int,
-                    device: int, concurrency: int | None = None, padded: bool = False) -> Meta:
-    bt, bn = preferred_tiles(hq=hq, hkv=hkv, d_qk=d_qk, d_v=d_v)
+                    device: int, concurrency: int | None = None, padded: bool = False,
+                    forward: bool = False) -> Meta:
+    """Metadata on a device with the kernels' tile sizes. forward=True picks the
+    forward's sizes for this batch (possibly 32-key tiles, which the backward
+    does not take); otherwise the sizes serve both directions."""
+    if forward:
+        bt, bn = preferred_fwd_tiles(seqlens=seqlens, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=d_qk,
+                                     d_v=d_v, padded=padded)
+    else:
+        bt, bn = preferred_tiles(hq=hq, hkv=hkv, d_qk=d_qk, d_v=d_v)
     if concurrency is None:
-        concurrency = device_concurrency(device, hkv)
+        concurrency = device_concurrency(device, hkv, bn)
     return build_metadata(seqlens=seqlens, cp=cp, rank=rank, block_t=bt, block_n=bn,
                           concurrency=concurrency, device=device, padded=padded)
 
@@ -309,7 +334,8 @@ def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=No
     device = q.device.index
     if meta is None:
         meta = device_metadata(seqlens=seqlens, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=d_qk,
-                               d_v=d_v, device=device, concurrency=concurrency, padded=padded)
+                               d_v=d_v, device=device, concurrency=concurrency, padded=padded,
+                               forward=True)
     inf = meta._cached_info()
     if q.shape[0] != inf["local_tokens"] or k.shape[0] != inf["total_tokens"] \
             or v.shape[0] != inf["total_tokens"]:
@@ -345,7 +371,9 @@ def attn_bwd(*, q, k, v, lse, d_o, seqlens, cp: int, rank: int, softmax_scale=No
     torch = _torch()
     hq, hkv, d_qk, d_v = q.shape[1], k.shape[1], q.shape[2], v.shape[2]
     device = q.device.index
-    if meta is None:
+    if meta is None or meta._cached_info()["block_n"] != preferred_tiles(
+            hq=hq, hkv=hkv, d_qk=d_qk, d_v=d_v)[1]:
+        # the backward kernels take the general tile sizes only
         meta = device_metadata(seqlens=seqlens, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=d_qk,
                                d_v=d_v, device=device, padded=padded)
     inf = meta._cached_info()

@@ -78,6 +78,12 @@ namespace thd {
 constexpr int kWaves = 4;
 constexpr int kRowsPerWg = 128;
 constexpr int kBlockN = 64;
+// The forward also runs 32-key tiles (d_qk <= 128), three workgroups per CU:
+// for batches of short documents, whose query tiles see few KV tiles.
+constexpr int kBlockNShort = 32;
+// Longest key range (in keys) of any query tile for which the forward prefers
+// 32-key tiles: eight 64-key tiles.
+constexpr int kShortKeyRange = 8 * kBlockN;
 
 struct FwdParams {
   const void* q;
@@ -92,7 +98,7 @@ struct FwdParams {
   const int32_t* splits;
   const int32_t* kv_row;
   const int32_t* doc_end;   // per document: one past its last real token
-  int32_t n_items, n_splits, hq, hkv, group, block_t;
+  int32_t n_items, n_splits, hq, hkv, group, block_t, block_n;
   int64_t total;
   float scale_log2;   // softmax_scale * log2(e)
 };
@@ -112,6 +118,8 @@ THD_HOST_DEVICE inline int64_t fwd_partial_floats(int32_t block_t, int32_t group
 
 // Kernel launchers (defined in the .hip files). Return a hipError_t value.
 int launch_fwd(const FwdParams& p, int d_qk, int d_v, void* stream);
+// Workgroups of the forward kernel for this KV tile size that fit one CU.
+int fwd_workgroups_per_cu(int block_n);
 
 struct BwdParams {
   const void* q;
@@ -143,5 +151,7 @@ inline int64_t bwd_ws_array_bytes(int64_t local, int32_t hq) {
 int launch_bwd(const BwdParams& p, int d_qk, int d_v, void* stream);
 bool bwd_supported(int d_qk, int d_v);
 bool fwd_supported(int d_qk, int d_v);
+// Whether the forward has a kernel for this KV tile size and d_qk.
+bool fwd_block_n_supported(int d_qk, int block_n);
 
 }  // namespace thd

@@ -160,13 +160,25 @@ void check_scale(float scale) {
   if (!(std::isfinite(scale) && scale > 0.0f)) fail(THD_EINVAL, "softmax_scale must be finite and > 0");
 }
 
-void check_tiles(const Plan& p, int32_t group) {
-  if (p.block_n != kBlockN)
-    fail(THD_EMISMATCH, "metadata block_n " + std::to_string(p.block_n) + " != kernel's " +
-                            std::to_string(kBlockN));
+void check_rows(const Plan& p, int32_t group) {
   if (int64_t(p.block_t) * group > kRowsPerWg)
     fail(THD_EMISMATCH, "metadata block_t " + std::to_string(p.block_t) + " times group " +
                             std::to_string(group) + " exceeds 128 rows");
+}
+
+void check_fwd_tiles(const Plan& p, int32_t group, int32_t d_qk) {
+  if (!fwd_block_n_supported(d_qk, p.block_n))
+    fail(THD_EMISMATCH, "metadata block_n " + std::to_string(p.block_n) +
+                            " has no forward kernel for d_qk=" + std::to_string(d_qk) +
+                            " (64, or 32 for d_qk <= 128)");
+  check_rows(p, group);
+}
+
+void check_bwd_tiles(const Plan& p, int32_t group) {
+  if (p.block_n != kBlockN)
+    fail(THD_EMISMATCH, "metadata block_n " + std::to_string(p.block_n) + " != backward kernels' " +
+                            std::to_string(kBlockN));
+  check_rows(p, group);
 }
 
 // The kernels address K and V with 32-bit byte offsets.
@@ -388,6 +400,44 @@ int thd_preferred_tiles(int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v, int3
   });
 }
 
+int thd_preferred_fwd_tiles(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank,
+                            int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v, int32_t* block_t,
+                            int32_t* block_n) {
+  return guarded([&] {
+    validate_partition(seqlens, n_docs, cp, rank);
+    check_heads(hq, hkv);
+    if (!fwd_supported(d_qk, d_v))
+      fail(THD_EUNSUPPORTED, "no kernel for d_qk=" + std::to_string(d_qk) +
+                                 ", d_v=" + std::to_string(d_v));
+    if (block_t == nullptr || block_n == nullptr) fail(THD_EINVAL, "output pointer is NULL");
+    // A rank's query tiles see at most (2cp - r) chunks of their document:
+    // the later chunk's tiles see every chunk up to their own.
+    int64_t longest = 0;
+    for (int32_t i = 0; i < n_docs; ++i)
+      longest = std::max(longest, int64_t(seqlens[i]) / (2 * cp) * (2 * cp - rank));
+    *block_t = preferred_block_t(hq / hkv);
+    *block_n = longest <= kShortKeyRange && fwd_block_n_supported(d_qk, kBlockNShort) ? kBlockNShort
+                                                                                      : kBlockN;
+  });
+}
+
+int thd_fwd_concurrency(int32_t device, int32_t hkv, int32_t block_n, int32_t* concurrency) {
+  return guarded([&] {
+    if (hkv < 1) fail(THD_EINVAL, "hkv must be >= 1");
+    if (block_n != kBlockN && block_n != kBlockNShort)
+      fail(THD_EINVAL, "block_n must be " + std::to_string(kBlockN) + " or " +
+                           std::to_string(kBlockNShort));
+    if (concurrency == nullptr) fail(THD_EINVAL, "concurrency is NULL");
+    int count = 0;
+    check_hip(hipGetDeviceCount(&count), "hipGetDeviceCount");
+    if (device < 0 || device >= count) fail(THD_EINVAL, "no such device " + std::to_string(device));
+    int cus = 0;
+    check_hip(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device),
+              "hipDeviceGetAttribute");
+    *concurrency = std::max(1, cus * fwd_workgroups_per_cu(block_n) / hkv);
+  });
+}
+
 int thd_attn_fwd_workspace(const thd_meta* meta, int32_t hq, int32_t hkv, int32_t d_v,
                            int64_t* bytes) {
   return guarded([&] {
@@ -413,7 +463,7 @@ int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void*
                                  ", d_v=" + std::to_string(d_v));
     check_scale(softmax_scale);
     const int32_t group = hq / hkv;
-    check_tiles(p, group);
+    check_fwd_tiles(p, group, d_qk);
     check_ptr(q, "q", 16);
     check_ptr(k, "k", 16);
     check_ptr(v, "v", 16);
@@ -451,6 +501,7 @@ int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void*
     fp.hkv = hkv;
     fp.group = group;
     fp.block_t = p.block_t;
+    fp.block_n = p.block_n;
     fp.total = p.total;
     fp.scale_log2 = softmax_scale * 1.4426950408889634f;
     check_hip(hipError_t(launch_fwd(fp, d_qk, d_v, hip_stream)), "forward launch");
@@ -480,7 +531,7 @@ int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void*
                                  ", d_v=" + std::to_string(d_v));
     check_scale(softmax_scale);
     const int32_t group = hq / hkv;
-    check_tiles(p, group);
+    check_bwd_tiles(p, group);
     check_ptr(q, "q", 16);
     check_ptr(k, "k", 16);
     check_ptr(v, "v", 16);

@@ -101,9 +101,9 @@ __device__ __forceinline__ int swz(int r) {
   }
 }
 
-template <int DQK, int DV>
+template <int DQK, int DV, int BN_>
 struct FwdShape {
-  static constexpr int BN = kBlockN;
+  static constexpr int BN = BN_;
   static constexpr int KCPR = DQK / 8;            // 16-byte chunks per K row
   static constexpr int VCPR = DV / 8;
   static constexpr int KROWB = DQK * 2;
@@ -130,9 +130,14 @@ struct FwdShape {
 // EXACT: P enters the PV product as a bf16 (hi, lo) pair and O is also written
 // in fp32 (p.o_f32): O is then exact up to fp32 accumulation, so the backward
 // can take D = rowsum(dO * O) from it.
-template <int DQK, int DV, bool EXACT>
-__global__ __launch_bounds__(kFwdThreads, 2) void thd_fwd_kernel(FwdParams p) {
-  using S = FwdShape<DQK, DV>;
+// Workgroups per CU: two with 64-key tiles (64 KB of LDS ring each), three
+// with 32-key tiles (the register budget then drops to 168 per lane).
+template <int BN>
+constexpr int kFwdOccupancy = BN == kBlockNShort ? 3 : 2;
+
+template <int DQK, int DV, bool EXACT, int BN_>
+__global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kernel(FwdParams p) {
+  using S = FwdShape<DQK, DV, BN_>;
   constexpr int BN = S::BN;
   constexpr int RB = kRowBlocks;
   // The two ring stages are separate arrays, and the tile loop is unrolled by
@@ -526,14 +531,14 @@ __global__ __launch_bounds__(256) void thd_fwd_combine_kernel(FwdParams p) {
   if (col == 0) p.lse[orow] = pad ? INFINITY : (mx + __builtin_amdgcn_logf(wsum)) * kLn2;
 }
 
-template <int DQK, int DV>
+template <int DQK, int DV, int BN>
 int launch(const FwdParams& p, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid(unsigned(int64_t(p.n_items) * p.hkv));
   if (p.o_f32 != nullptr) {
-    hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV, true>), grid, dim3(kFwdThreads), 0, st, p);
+    hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV, true, BN>), grid, dim3(kFwdThreads), 0, st, p);
   } else {
-    hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV, false>), grid, dim3(kFwdThreads), 0, st, p);
+    hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV, false, BN>), grid, dim3(kFwdThreads), 0, st, p);
   }
   hipError_t err = hipGetLastError();
   if (err != hipSuccess || p.n_splits == 0) return int(err);
@@ -549,10 +554,23 @@ bool fwd_supported(int d_qk, int d_v) {
   return (d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128);
 }
 
+bool fwd_block_n_supported(int d_qk, int block_n) {
+  // 32-key tiles are not built for d_qk = 192: at 168 registers per lane the
+  // MLA kernel spills.
+  return block_n == kBlockN || (block_n == kBlockNShort && d_qk <= 128);
+}
+
+int fwd_workgroups_per_cu(int block_n) {
+  return block_n == kBlockNShort ? kFwdOccupancy<kBlockNShort> : kFwdOccupancy<kBlockN>;
+}
+
 int launch_fwd(const FwdParams& p, int d_qk, int d_v, void* stream) {
-  if (d_qk == 64 && d_v == 64) return launch<64, 64>(p, stream);
-  if (d_qk == 128 && d_v == 128) return launch<128, 128>(p, stream);
-  if (d_qk == 192 && d_v == 128) return launch<192, 128>(p, stream);
+  const bool short_tiles = p.block_n == kBlockNShort;
+  if (d_qk == 64 && d_v == 64)
+    return short_tiles ? launch<64, 64, kBlockNShort>(p, stream) : launch<64, 64, kBlockN>(p, stream);
+  if (d_qk == 128 && d_v == 128)
+    return short_tiles ? launch<128, 128, kBlockNShort>(p, stream) : launch<128, 128, kBlockN>(p, stream);
+  if (d_qk == 192 && d_v == 128 && !short_tiles) return launch<192, 128, kBlockN>(p, stream);
   return int(hipErrorInvalidValue);
 }
 

@@ -10,4 +10,6 @@ int launch_fwd(const FwdParams&, int, int, void*) { return int(hipErrorInvalidVa
 int launch_bwd(const BwdParams&, int, int, void*) { return int(hipErrorInvalidValue); }
 bool fwd_supported(int, int) { return false; }
 bool bwd_supported(int, int) { return false; }
+bool fwd_block_n_supported(int, int) { return false; }
+int fwd_workgroups_per_cu(int) { return 1; }
 }  // namespace thd

@@ -94,6 +94,32 @@ def test_forward_split_key_ranges_match_oracle(case, concurrency):
     assert (lse - lse1).abs().max().item() <= 1e-4
 
 
+@pytest.mark.parametrize("case", [c for c in SMALL + SPLIT if c[6] <= 128], ids=lambda c: f"seed{c[0]}")
+@pytest.mark.parametrize("concurrency", [0, 64])
+def test_forward_short_tiles_match_oracle(case, concurrency):
+    """The 32-key-tile kernels (three workgroups per CU), with and without split
+    key ranges, in both P paths: O, LSE and the exact fp32 O against the oracle."""
+    seed, lengths, cp, rank, hq, hkv, dqk, dv = case
+    b = workloads.small_case(seed, lengths, cp, hq, hkv, dqk, dv, rank=rank)
+    dev = device()
+    q, k, v = b.q.to(dev), b.k.to(dev), b.v.to(dev)
+    bt = thd.preferred_tiles(hq=hq, hkv=hkv, d_qk=dqk, d_v=dv)[0]
+    meta = thd.build_metadata(seqlens=b.lengths, cp=cp, rank=rank, block_t=bt, block_n=32,
+                              concurrency=concurrency, device=0)
+    print(f"[fwd short tiles] seed={seed} concurrency={concurrency} "
+          f"splits={meta.info()['n_splits']}", flush=True)
+    want_o, want_lse = oatt.attn_fwd64(to64(b.q), to64(b.k), to64(b.v), lengths, cp, rank)
+    o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=b.lengths, cp=cp, rank=rank, meta=meta)
+    o32 = torch.full((q.shape[0], hq, dv), float("nan"), dtype=torch.float32, device=dev)
+    o_x, lse_x = thd.attn_fwd(q=q, k=k, v=v, seqlens=b.lengths, cp=cp, rank=rank, meta=meta,
+                              out_f32=o32)
+    torch.cuda.synchronize()
+    assert_close(to64(o), want_o, "O")
+    assert_close(lse.cpu().double().numpy(), want_lse, "LSE", max_abs=LSE_ABS, mean_abs=LSE_ABS)
+    assert_close(to64(o32), want_o, "O32", max_abs=O32_ABS, mean_abs=O32_ABS / 10)
+    assert_close(to64(o_x), want_o, "O (exact path)")
+
+
 def test_split_forward_and_backward_on_side_streams():
     """Calls on two side streams at once (split forward, whose partial results
     need a workspace, then the backward) give bit-identical results to the same

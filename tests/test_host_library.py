@@ -100,6 +100,56 @@ def test_preferred_tiles():
     assert thd.preferred_tiles(hq=12, hkv=4, d_qk=128, d_v=128) == (42, 64)
 
 
+def test_preferred_fwd_tiles_follow_the_longest_key_range():
+    """32-key tiles when no query tile sees more than 512 keys: the later chunk
+    of rank r sees (2cp - r) chunks, i.e. (2cp - r) * L / (2cp) keys."""
+    heads = dict(hq=64, hkv=8, d_qk=128, d_v=128)
+    # cp 8, rank 0: the later chunk sees all 16 chunks, L keys
+    assert thd.preferred_fwd_tiles(seqlens=[512, 16], cp=8, rank=0, **heads) == (16, 32)
+    assert thd.preferred_fwd_tiles(seqlens=[528, 16], cp=8, rank=0, **heads) == (16, 64)
+    # rank 7 sees 9 of 16 chunks: 576 * 9 / 16 = 324 keys
+    assert thd.preferred_fwd_tiles(seqlens=[576], cp=8, rank=7, **heads) == (16, 32)
+    assert thd.preferred_fwd_tiles(seqlens=[912], cp=8, rank=7, **heads) == (16, 64)
+    # every workload keeps 64-key tiles except the short-document one
+    for w in workloads.WORKLOADS:
+        lengths = workloads.draw_lengths(w, np.random.default_rng(w.index))
+        bt, bn = thd.preferred_fwd_tiles(seqlens=lengths, cp=w.cp, rank=w.rank, hq=w.hq,
+                                         hkv=w.hkv, d_qk=w.d_qk, d_v=w.d_v)
+        assert bt == thd.preferred_tiles(hq=w.hq, hkv=w.hkv, d_qk=w.d_qk, d_v=w.d_v)[0]
+        assert bn == (32 if w.name in ("short", "tiny") else 64), w.name
+    # no 32-key kernel for d_qk = 192
+    assert thd.preferred_fwd_tiles(seqlens=[64], cp=1, rank=0, hq=16, hkv=16, d_qk=192,
+                                   d_v=128) == (128, 64)
+    # padded layout: the padded lengths count
+    assert thd.preferred_fwd_tiles(seqlens=[512], cp=8, rank=0, padded=True, **heads) == (16, 32)
+    assert thd.preferred_fwd_tiles(seqlens=[513], cp=8, rank=0, padded=True, **heads) == (16, 64)
+    with pytest.raises(thd.ThdError) as err:
+        thd.preferred_fwd_tiles(seqlens=[6], cp=2, rank=0, **heads)
+    assert err.value.status == "THD_ENOTDIV"
+
+
+def test_short_tile_metadata_is_refused_where_it_has_no_kernel():
+    """Metadata with 32-key tiles serves the forward for d_qk <= 128 only: the
+    backward and the d_qk = 192 forward refuse it before any device check."""
+    m = thd.build_metadata(seqlens=[256], cp=1, rank=0, block_t=32, block_n=32)
+    buf = ctypes.create_string_buffer(1 << 16)
+    ptr = (ctypes.addressof(buf) + 15) // 16 * 16
+    lib = thd._lib
+    assert lib.thd_attn_bwd(m.handle, ptr, ptr, ptr, ptr, None, ptr, ptr, ptr, ptr, 32, 8, 128,
+                            128, 0.1, ptr, 1 << 16, None) == -5
+    assert b"block_n" in lib.thd_last_error()
+    m192 = thd.build_metadata(seqlens=[256], cp=1, rank=0, block_t=128, block_n=32)
+    assert lib.thd_attn_fwd(m192.handle, ptr, ptr, ptr, ptr, ptr, None, 16, 16, 192, 128, 0.1,
+                            None, 0, None) == -5
+    # 32-key metadata reaches the device check for d_qk = 128 (host-only copy here)
+    assert lib.thd_attn_fwd(m.handle, ptr, ptr, ptr, ptr, ptr, None, 32, 8, 128, 128, 0.1,
+                            None, 0, None) == -5
+    assert b"device copy" in lib.thd_last_error()
+    c = ctypes.c_int32()
+    assert lib.thd_fwd_concurrency(0, 8, 48, ctypes.byref(c)) == -1
+    assert lib.thd_fwd_concurrency(0, 0, 64, ctypes.byref(c)) == -1
+
+
 @pytest.mark.parametrize("kwargs,status", [
     (dict(seqlens=[6, 8], cp=2, rank=0), "THD_ENOTDIV"),
     (dict(seqlens=[8], cp=2, rank=2), "THD_ERANGE"),
