@@ -430,50 +430,68 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
     if (j + 1 < kv_end) step(j + 1, smem1, smem0);
   }
 
-#pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    if (!rb_active[rb]) continue;
-    const float l_tot = l_run[rb] + __shfl_xor(l_run[rb], 32);
-    if (!valid[rb]) continue;
-    const float inv = 1.0f / l_tot;
-    if (part >= 0) {
-      // Part of a split tile: its O normalised by its own sum, and its
-      // log2-sum-exp, for the combine kernel.
-      const int rows = p.block_t * G;
-      const int row = 32 * (RB * wave + rb) + lrow;
-      float* base = p.partial + (size_t(part) * p.hkv + kvh) * size_t(fwd_partial_floats(p.block_t, G, DV));
-      float* orow = base + size_t(row) * DV;
-#pragma unroll
-      for (int b = 0; b < S::DVB; ++b)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          f32x4 out;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) out[e] = acc[rb][b][4 * g + e] * inv;
-          *reinterpret_cast<f32x4*>(orow + 32 * b + 8 * g + 4 * half) = out;
-        }
-      if (half == 0) base[size_t(rows) * DV + row] = m_run[rb] + __builtin_amdgcn_logf(l_tot);
-      continue;
-    }
-    const size_t orow_idx = size_t(q_local0 + tok[rb]) * p.hq + head[rb];
-    __bf16* orow = static_cast<__bf16*>(p.o) + orow_idx * DV;
-    const bool real = tok[rb] < n_real;   // pad rows get O = 0
+  static_assert(RB == 1, "the epilogue stages one 32-row block per wave");
+  if (!wave_active) return;
+  const float l_tot = l_run[0] + __shfl_xor(l_run[0], 32);
+  const float inv = 1.0f / l_tot;
+  if (part >= 0) {
+    // Part of a split tile: its O normalised by its own sum, and its
+    // log2-sum-exp, for the combine kernel.
+    if (!valid[0]) return;
+    const int rows = p.block_t * G;
+    const int row = 32 * wave + lrow;
+    float* base = p.partial + (size_t(part) * p.hkv + kvh) * size_t(fwd_partial_floats(p.block_t, G, DV));
+    float* orow = base + size_t(row) * DV;
 #pragma unroll
     for (int b = 0; b < S::DVB; ++b)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
-        f32x4 o4;
-        bf16x4 out;
+        f32x4 out;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          o4[e] = real ? acc[rb][b][4 * g + e] * inv : 0.0f;
-          out[e] = static_cast<__bf16>(o4[e]);
-        }
-        *reinterpret_cast<bf16x4*>(orow + 32 * b + 8 * g + 4 * half) = out;
-        if constexpr (EXACT) *reinterpret_cast<f32x4*>(p.o_f32 + orow_idx * DV + 32 * b + 8 * g + 4 * half) = o4;
+        for (int e = 0; e < 4; ++e) out[e] = acc[0][b][4 * g + e] * inv;
+        *reinterpret_cast<f32x4*>(orow + 32 * b + 8 * g + 4 * half) = out;
       }
-    if (half == 0)
-      p.lse[orow_idx] = real ? (m_run[rb] + __builtin_amdgcn_logf(l_tot)) * kLn2 : INFINITY;
+    if (half == 0) base[size_t(rows) * DV + row] = m_run[0] + __builtin_amdgcn_logf(l_tot);
+    return;
+  }
+  // O leaves through LDS: each lane holds 4 columns of one row per (b, g),
+  // which as global stores would write 16 bytes per row per instruction. The
+  // wave writes its 32 rows into its own part of the ring (free once the last
+  // tile's barrier has passed), 16-byte chunks XOR-swizzled by row, then
+  // stores whole rows, 16 bytes per lane.
+  const bool real = tok[0] < n_real;   // pad rows get O = 0
+  char* region = (wave < 2 ? smem0 : smem1) + (wave & 1) * (32 * S::VROWB);
+  const size_t orow_idx = size_t(q_local0 + tok[0]) * p.hq + head[0];
+#pragma unroll
+  for (int b = 0; b < S::DVB; ++b)
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      f32x4 o4;
+      bf16x4 out;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        o4[e] = real ? acc[0][b][4 * g + e] * inv : 0.0f;
+        out[e] = static_cast<__bf16>(o4[e]);
+      }
+      const int chunk = (4 * b + g) ^ (lrow & (S::VCPR - 1));
+      *reinterpret_cast<bf16x4*>(region + lrow * S::VROWB + chunk * 16 + half * 8) = out;
+      if constexpr (EXACT)
+        if (valid[0]) *reinterpret_cast<f32x4*>(p.o_f32 + orow_idx * DV + 32 * b + 8 * g + 4 * half) = o4;
+    }
+  if (half == 0 && valid[0])
+    p.lse[orow_idx] = real ? (m_run[0] + __builtin_amdgcn_logf(l_tot)) * kLn2 : INFINITY;
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __bf16* __restrict__ obase = static_cast<__bf16*>(p.o);
+#pragma unroll
+  for (int i = 0; i < 32 * S::VCPR / 64; ++i) {
+    const int q = i * 64 + lane;
+    const int r = q / S::VCPR;           // row within the wave's block
+    const int c = q % S::VCPR;           // 16-byte chunk of the row
+    const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(region + r * S::VROWB + ((c ^ (r & (S::VCPR - 1))) << 4));
+    const int tok_r = __shfl(tok[0], r);
+    const int head_r = __shfl(head[0], r);
+    if (tok_r < n_rows)
+      *reinterpret_cast<bf16x8*>(obase + (size_t(q_local0 + tok_r) * p.hq + head_r) * DV + 8 * c) = v8;
   }
 }
 
