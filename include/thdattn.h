@@ -193,12 +193,14 @@ int thd_preferred_tiles(int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
 
 /* Tile sizes for the forward of one batch (seqlens[n_docs] as laid out, i.e.
  * padded lengths for the padded layout; host). The forward also has 32-key
- * tile kernels for d_qk <= 128, run three workgroups per CU instead of two:
- * chosen (block_n = 32) when no query tile of this rank sees more than 512
- * keys, i.e. (2cp - rank) * L_i / (2cp) <= 512 for every document, else
- * block_n = 64. block_t as thd_preferred_tiles. Metadata built with block_n =
- * 32 serves thd_attn_fwd only: thd_attn_bwd needs block_n = 64 (THD_EMISMATCH
- * otherwise). Errors as thd_plan_partition, plus THD_EUNSUPPORTED. */
+ * tile kernels for d_qk <= 128, run three workgroups per CU instead of two.
+ * They are chosen (block_n = 32) when they compute at least 7% fewer key
+ * slots than 64-key tiles: a query tile visits its document's keys up to its
+ * last row, rounded up to whole KV tiles, so short chunks leave most of a
+ * 64-key tile masked. Otherwise block_n = 64. block_t as thd_preferred_tiles.
+ * Metadata built with block_n = 32 serves thd_attn_fwd only: thd_attn_bwd
+ * needs block_n = 64 (THD_EMISMATCH otherwise). Errors as
+ * thd_plan_partition, plus THD_EUNSUPPORTED. */
 int thd_preferred_fwd_tiles(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank,
                             int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v, int32_t* block_t,
                             int32_t* block_n);

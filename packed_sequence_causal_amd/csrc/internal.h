@@ -81,9 +81,6 @@ constexpr int kBlockN = 64;
 // The forward also runs 32-key tiles (d_qk <= 128), three workgroups per CU:
 // for batches of short documents, whose query tiles see few KV tiles.
 constexpr int kBlockNShort = 32;
-// Longest key range (in keys) of any query tile for which the forward prefers
-// 32-key tiles: eight 64-key tiles.
-constexpr int kShortKeyRange = 8 * kBlockN;
 
 struct FwdParams {
   const void* q;

@@ -410,14 +410,29 @@ int thd_preferred_fwd_tiles(const int32_t* seqlens, int32_t n_docs, int32_t cp, 
       fail(THD_EUNSUPPORTED, "no kernel for d_qk=" + std::to_string(d_qk) +
                                  ", d_v=" + std::to_string(d_v));
     if (block_t == nullptr || block_n == nullptr) fail(THD_EINVAL, "output pointer is NULL");
-    // A rank's query tiles see at most (2cp - r) chunks of their document:
-    // the later chunk's tiles see every chunk up to their own.
-    int64_t longest = 0;
-    for (int32_t i = 0; i < n_docs; ++i)
-      longest = std::max(longest, int64_t(seqlens[i]) / (2 * cp) * (2 * cp - rank));
-    *block_t = preferred_block_t(hq / hkv);
-    *block_n = longest <= kShortKeyRange && fwd_block_n_supported(d_qk, kBlockNShort) ? kBlockNShort
-                                                                                      : kBlockN;
+    // Key slots the forward computes (visited KV tiles times their size) with
+    // 64- and with 32-key tiles: query tile t0.. of chunk k sees the document's
+    // keys up to k*c + t0 + rows. Short tiles pay when they drop more than 7%
+    // of the slots (keys past each tile's last row that a 64-key tile still
+    // computes); below that their extra barriers and the tighter register
+    // budget of the third workgroup cost more than they save.
+    const int32_t bt = preferred_block_t(hq / hkv);
+    int64_t slots64 = 0, slots32 = 0;
+    for (int32_t i = 0; i < n_docs; ++i) {
+      const int64_t c = seqlens[i] / (2 * cp);
+      for (int s = 0; s < 2; ++s) {
+        const int64_t k = s == 0 ? rank : 2 * cp - 1 - rank;
+        for (int64_t t0 = 0; t0 < c; t0 += bt) {
+          const int64_t kv_len = k * c + t0 + std::min<int64_t>(bt, c - t0);
+          slots64 += (kv_len + kBlockN - 1) / kBlockN * kBlockN;
+          slots32 += (kv_len + kBlockNShort - 1) / kBlockNShort * kBlockNShort;
+        }
+      }
+    }
+    *block_t = bt;
+    *block_n = fwd_block_n_supported(d_qk, kBlockNShort) && 100 * slots32 <= 93 * slots64
+                   ? kBlockNShort
+                   : kBlockN;
   });
 }
 

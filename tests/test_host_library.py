@@ -100,29 +100,53 @@ def test_preferred_tiles():
     assert thd.preferred_tiles(hq=12, hkv=4, d_qk=128, d_v=128) == (42, 64)
 
 
-def test_preferred_fwd_tiles_follow_the_longest_key_range():
-    """32-key tiles when no query tile sees more than 512 keys: the later chunk
-    of rank r sees (2cp - r) chunks, i.e. (2cp - r) * L / (2cp) keys."""
+def _key_slots(lengths, cp, rank, bt, bn):
+    """Key slots a forward with bn-key tiles computes: each query tile visits
+    its document's keys up to its last row, in whole KV tiles."""
+    total = 0
+    for length in lengths:
+        c = length // (2 * cp)
+        for k in (rank, 2 * cp - 1 - rank):
+            for t0 in range(0, c, bt):
+                kv_len = k * c + t0 + min(bt, c - t0)
+                total += -(-kv_len // bn) * bn
+    return total
+
+
+def test_preferred_fwd_tiles_pick_short_tiles_when_they_save_key_slots():
+    """32-key tiles when they compute at least 7% fewer key slots than 64-key
+    tiles (d_qk <= 128 only); block_t as for the general tile sizes."""
+    rng = np.random.default_rng(77)
+    for _ in range(40):
+        cp = int(rng.choice([1, 2, 4, 8]))
+        lengths = workloads.random_lengths(rng, int(rng.integers(1, 12)), cp, 48)
+        rank = int(rng.integers(0, cp))
+        g = int(rng.choice([1, 4, 8]))
+        bt = 128 // g
+        want = 32 if 100 * _key_slots(lengths, cp, rank, bt, 32) <= 93 * _key_slots(
+            lengths, cp, rank, bt, 64) else 64
+        got = thd.preferred_fwd_tiles(seqlens=lengths, cp=cp, rank=rank, hq=8 * g, hkv=8,
+                                      d_qk=128, d_v=128)
+        assert got == (bt, want), (lengths, cp, rank, g)
     heads = dict(hq=64, hkv=8, d_qk=128, d_v=128)
-    # cp 8, rank 0: the later chunk sees all 16 chunks, L keys
+    # a one-token chunk next to a 32-token one: most of each 64-key tile is masked
     assert thd.preferred_fwd_tiles(seqlens=[512, 16], cp=8, rank=0, **heads) == (16, 32)
-    assert thd.preferred_fwd_tiles(seqlens=[528, 16], cp=8, rank=0, **heads) == (16, 64)
-    # rank 7 sees 9 of 16 chunks: 576 * 9 / 16 = 324 keys
-    assert thd.preferred_fwd_tiles(seqlens=[576], cp=8, rank=7, **heads) == (16, 32)
-    assert thd.preferred_fwd_tiles(seqlens=[912], cp=8, rank=7, **heads) == (16, 64)
-    # every workload keeps 64-key tiles except the short-document one
+    # chunks of whole 64-key tiles save nothing
+    assert thd.preferred_fwd_tiles(seqlens=[512] * 4, cp=4, rank=2, hq=32, hkv=8, d_qk=128,
+                                   d_v=128) == (32, 64)
+    # of the workloads only the short-document one takes 32-key tiles
     for w in workloads.WORKLOADS:
         lengths = workloads.draw_lengths(w, np.random.default_rng(w.index))
         bt, bn = thd.preferred_fwd_tiles(seqlens=lengths, cp=w.cp, rank=w.rank, hq=w.hq,
                                          hkv=w.hkv, d_qk=w.d_qk, d_v=w.d_v)
         assert bt == thd.preferred_tiles(hq=w.hq, hkv=w.hkv, d_qk=w.d_qk, d_v=w.d_v)[0]
-        assert bn == (32 if w.name in ("short", "tiny") else 64), w.name
+        assert bn == (32 if w.name == "short" else 64), w.name
     # no 32-key kernel for d_qk = 192
-    assert thd.preferred_fwd_tiles(seqlens=[64], cp=1, rank=0, hq=16, hkv=16, d_qk=192,
+    assert thd.preferred_fwd_tiles(seqlens=[512, 16], cp=8, rank=0, hq=16, hkv=16, d_qk=192,
                                    d_v=128) == (128, 64)
-    # padded layout: the padded lengths count
-    assert thd.preferred_fwd_tiles(seqlens=[512], cp=8, rank=0, padded=True, **heads) == (16, 32)
-    assert thd.preferred_fwd_tiles(seqlens=[513], cp=8, rank=0, padded=True, **heads) == (16, 64)
+    # padded layout: the padded lengths count (17 real tokens -> 32 with cp 8)
+    assert thd.preferred_fwd_tiles(seqlens=[512, 1], cp=8, rank=0, padded=True,
+                                   **heads) == (16, 32)
     with pytest.raises(thd.ThdError) as err:
         thd.preferred_fwd_tiles(seqlens=[6], cp=2, rank=0, **heads)
     assert err.value.status == "THD_ENOTDIV"
