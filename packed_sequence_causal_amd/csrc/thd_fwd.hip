@@ -320,17 +320,31 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
             }
         }
 
-        // This lane's half of the row maximum, as a tree (short chains).
+        // This lane's half of the row maximum, as a tree of three-input maxima
+        // (v_max3_f32: 32 values in 16 instructions, short chains).
         constexpr int NV = 16 * S::KB;
         float mv[NV];
 #pragma unroll
         for (int kb2 = 0; kb2 < S::KB; ++kb2)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mv[16 * kb2 + r] = s[rb][kb2][r];
+        int nv = NV;
 #pragma unroll
-        for (int w = NV / 2; w >= 1; w /= 2)
+        for (int round = 0; round < 6; ++round) {
+          if (nv <= 1) break;
+          const int n3 = nv / 3, rem = nv - 3 * n3;
 #pragma unroll
-          for (int i = 0; i < w; ++i) mv[i] = fmaxf(mv[i], mv[i + w]);
+          for (int i = 0; i < n3; ++i) mv[i] = fmaxf(mv[3 * i], fmaxf(mv[3 * i + 1], mv[3 * i + 2]));
+          if (rem == 2) {
+            mv[n3] = fmaxf(mv[3 * n3], mv[3 * n3 + 1]);
+            nv = n3 + 1;
+          } else if (rem == 1) {
+            mv[n3] = mv[3 * n3];
+            nv = n3 + 1;
+          } else {
+            nv = n3;
+          }
+        }
         const float m_half = mv[0] * c2;
         // A row is rescaled only when its maximum grows by more than the slack,
         // which a row can only do if one of its halves does: only then do the
