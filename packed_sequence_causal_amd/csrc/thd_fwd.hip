@@ -70,6 +70,9 @@ constexpr int kFwdThreads = kFwdWaves * 64;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleSlack = 8.0f;
 constexpr int kWaitVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;    // s_waitcnt lgkmcnt(0)
+template <int N>
+constexpr int kWaitLgkmKB = 0xC07F | (N << 8);   // s_waitcnt lgkmcnt(N)
 
 // 16-byte global -> LDS copy: lane i's 16 bytes land at lds + 16 * i (lds is
 // wave-uniform). Kept as a function taking a named pointer: handing the
@@ -292,15 +295,45 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int kb2 = 0; kb2 < S::KB; ++kb2) s[rb][kb2] = f32x16{};
+      if constexpr (BN == kBlockN) {
+        // K fragments one k-step ahead: the reads of step st + 1 are in flight
+        // while step st's MFMAs run (the partial wait leaves them outstanding).
+        // Not for 32-key tiles: at their register budget the extra fragments
+        // cost more than the overlap gains.
+        bf16x8 ka[2][S::KB];
 #pragma unroll
-      for (int st = 0; st < S::KSTEPS; ++st) {
-        const int cpos = ((2 * st + half) ^ k_swz) * 16;
+        for (int kb2 = 0; kb2 < S::KB; ++kb2)
+          ka[0][kb2] = *reinterpret_cast<const bf16x8*>(stage + k_off + 32 * kb2 * S::KROWB + ((half ^ k_swz) * 16));
 #pragma unroll
-        for (int kb2 = 0; kb2 < S::KB; ++kb2) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + k_off + 32 * kb2 * S::KROWB + cpos);
+        for (int st = 0; st < S::KSTEPS; ++st) {
+          if (st + 1 < S::KSTEPS) {
+            const int cpos = ((2 * (st + 1) + half) ^ k_swz) * 16;
 #pragma unroll
-          for (int rb = 0; rb < RB; ++rb)
-            if (rb_active[rb]) s[rb][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][st], s[rb][kb2], 0, 0, 0);
+            for (int kb2 = 0; kb2 < S::KB; ++kb2)
+              ka[(st + 1) & 1][kb2] = *reinterpret_cast<const bf16x8*>(stage + k_off + 32 * kb2 * S::KROWB + cpos);
+            __builtin_amdgcn_s_waitcnt(kWaitLgkmKB<S::KB>);   // this step's reads have landed
+          } else {
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int kb2 = 0; kb2 < S::KB; ++kb2)
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              if (rb_active[rb]) s[rb][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st & 1][kb2], qf[rb][st], s[rb][kb2], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int st = 0; st < S::KSTEPS; ++st) {
+          const int cpos = ((2 * st + half) ^ k_swz) * 16;
+#pragma unroll
+          for (int kb2 = 0; kb2 < S::KB; ++kb2) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(stage + k_off + 32 * kb2 * S::KROWB + cpos);
+#pragma unroll
+            for (int rb = 0; rb < RB; ++rb)
+              if (rb_active[rb]) s[rb][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[rb][st], s[rb][kb2], 0, 0, 0);
+          }
         }
       }
 
