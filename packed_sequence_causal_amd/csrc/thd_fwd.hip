@@ -295,11 +295,12 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
       for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
         for (int kb2 = 0; kb2 < S::KB; ++kb2) s[rb][kb2] = f32x16{};
-      if constexpr (BN == kBlockN) {
+      if constexpr (BN == kBlockN && DQK <= 128) {
         // K fragments one k-step ahead: the reads of step st + 1 are in flight
         // while step st's MFMAs run (the partial wait leaves them outstanding).
-        // Not for 32-key tiles: at their register budget the extra fragments
-        // cost more than the overlap gains.
+        // Not for 32-key tiles, nor for d_qk = 192, whose twelve Q fragments
+        // leave no room: there the extra fragments spill or cost more than the
+        // overlap gains.
         bf16x8 ka[2][S::KB];
 #pragma unroll
         for (int kb2 = 0; kb2 < S::KB; ++kb2)
