@@ -266,8 +266,12 @@ __global__ __launch_bounds__(kWaves * 64, DQK > 128 ? 1 : 2) void thd_bwd_dq_ker
           dp[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, df[st], dp[kb2], 0, 0, 0);
         }
       }
-      const bool masked = j >= n_full;
+      // Key key0 + off lies past this lane's row exactly when off > lim; lim
+      // is INT_MAX on tiles before n_full, which every row sees whole (and
+      // qpos - key0 cannot overflow: key0 >= 0). The offsets are inline
+      // constants, so the test is one compare and one select per element.
       const int key0 = kv_start + j * BN + 4 * half;
+      const int lim = j >= n_full ? qpos - key0 : INT_MAX;
       // dS as a bf16 pair (hi + lo): its rounding stays ~2^-16 relative.
       u32x4 dsh4[4], dsl4[4];
 #pragma unroll
@@ -277,9 +281,8 @@ __global__ __launch_bounds__(kWaves * 64, DQK > 128 ? 1 : 2) void thd_bwd_dq_ker
           float pr[2], ds[2];
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const int key = key0 + 32 * kb2 + 8 * ((r + e) >> 2) + ((r + e) & 3);
             pr[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb2][r + e], c2, -lse2));
-            if (masked && key > qpos) pr[e] = 0.0f;
+            if (32 * kb2 + 8 * ((r + e) >> 2) + ((r + e) & 3) > lim) pr[e] = 0.0f;
             if constexpr (DELTA) {
               dsum = __builtin_fmaf(pr[e], dp[kb2][r + e], dsum);
             } else {
