@@ -60,6 +60,8 @@ typedef __attribute__((address_space(4))) const int32_t cint32_t;
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kWaitVmcnt0 = 0x0F70;   // s_waitcnt vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;    // s_waitcnt lgkmcnt(0)
+constexpr int kWaitLgkm1 = 0xC17F;    // s_waitcnt lgkmcnt(1)
 constexpr int BN = kBlockN;
 
 // 16-byte global -> LDS copy: lane i's 16 bytes land at lds + 16 * i (lds is
@@ -122,6 +124,20 @@ struct DqShape {
   static constexpr bool SAME_ROWS = (KCPR == VCPR);
   static constexpr int NROWS = SAME_ROWS ? K_IPW : K_IPW + V_IPW;
   static constexpr int KSTEPS = DQK / 16, VSTEPS = DV / 16, DQB = DQK / 32;
+  // Products of S^T and dP^T in issue order: operand n = 4 * step + w, with
+  // w = (K, keys 0-31), (V, keys 0-31), (K, keys 32-63), (V, keys 32-63).
+  static constexpr int NSTEPS = KSTEPS > VSTEPS ? KSTEPS : VSTEPS;
+  static constexpr bool has_op(int n) { return (n & 1) ? (n >> 2) < VSTEPS : (n >> 2) < KSTEPS; }
+  static constexpr int next_op(int n) {
+    for (int m = n + 1; m < 4 * NSTEPS; ++m)
+      if (has_op(m)) return m;
+    return -1;
+  }
+  static constexpr int op_index(int n) {
+    int k = 0;
+    for (int m = 0; m < n; ++m) k += has_op(m) ? 1 : 0;
+    return k;
+  }
 };
 
 template <int DQK, int DV, bool DELTA>
@@ -250,20 +266,57 @@ __global__ __launch_bounds__(kWaves * 64, DQK > 128 ? 1 : 2) void thd_bwd_dq_ker
     if (wave_active) {
       f32x16 s[2] = {f32x16{}, f32x16{}};
       f32x16 dp[2] = {f32x16{}, f32x16{}};
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const int r = 32 * kb2 + lrow;
-#pragma unroll
-        for (int st = 0; st < S::KSTEPS; ++st) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+      // The four products (K and V of each 32-key half) advance one k-step at
+      // a time, and each operand is read from LDS one product ahead of its
+      // MFMA: the partial wait leaves that read in flight while the MFMA
+      // issues, instead of exposing every read's latency. Not at d_qk = 192,
+      // where the second operand buffer spills.
+      if constexpr (DQK <= 128) {
+        auto frag = [&](int n) -> bf16x8 {
+          const int st = n >> 2, w = n & 3, r = 32 * (w >> 1) + lrow;
+          if (w & 1)
+            return *reinterpret_cast<const bf16x8*>(
+                stage + S::KBYTES + r * S::VROWB + (((2 * st + half) ^ swz<S::VCPR>(r)) << 4));
+          return *reinterpret_cast<const bf16x8*>(
               stage + r * S::KROWB + (((2 * st + half) ^ swz<S::KCPR>(r)) << 4));
-          s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb2], 0, 0, 0);
-        }
+        };
+        bf16x8 fb[2];
+        fb[0] = frag(0);
 #pragma unroll
-        for (int st = 0; st < S::VSTEPS; ++st) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(
-              stage + S::KBYTES + r * S::VROWB + (((2 * st + half) ^ swz<S::VCPR>(r)) << 4));
-          dp[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, df[st], dp[kb2], 0, 0, 0);
+        for (int n = 0; n < 4 * S::NSTEPS; ++n) {
+          if (!S::has_op(n)) continue;
+          const int nx = S::next_op(n);
+          if (nx >= 0) {
+            fb[(S::op_index(n) + 1) & 1] = frag(nx);
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm1);
+          } else {
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+          }
+          __builtin_amdgcn_sched_barrier(0);
+          const int st = n >> 2, w = n & 3;
+          const bf16x8 a = fb[S::op_index(n) & 1];
+          if (w & 1)
+            dp[w >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, df[st], dp[w >> 1], 0, 0, 0);
+          else
+            s[w >> 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[w >> 1], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      } else {
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          const int r = 32 * kb2 + lrow;
+#pragma unroll
+          for (int st = 0; st < S::KSTEPS; ++st) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                stage + r * S::KROWB + (((2 * st + half) ^ swz<S::KCPR>(r)) << 4));
+            s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[st], s[kb2], 0, 0, 0);
+          }
+#pragma unroll
+          for (int st = 0; st < S::VSTEPS; ++st) {
+            const bf16x8 a = *reinterpret_cast<const bf16x8*>(
+                stage + S::KBYTES + r * S::VROWB + (((2 * st + half) ^ swz<S::VCPR>(r)) << 4));
+            dp[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, df[st], dp[kb2], 0, 0, 0);
+          }
         }
       }
       // Key key0 + off lies past this lane's row exactly when off > lim; lim
