@@ -324,7 +324,8 @@ __global__ __launch_bounds__(kWaves * 64, DQK > 128 ? 1 : 2) void thd_bwd_dq_ker
       // qpos - key0 cannot overflow: key0 >= 0). The offsets are inline
       // constants, so the test is one compare and one select per element.
       const int key0 = kv_start + j * BN + 4 * half;
-      const int lim = j >= n_full ? qpos - key0 : INT_MAX;
+      int lim = j >= n_full ? qpos - key0 : INT_MAX;
+      asm volatile("" : "+v"(lim));   // one register, not a tile flag ANDed into every compare
       // dS as a bf16 pair (hi + lo): its rounding stays ~2^-16 relative.
       u32x4 dsh4[4], dsl4[4];
 #pragma unroll
