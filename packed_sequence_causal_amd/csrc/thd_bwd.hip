@@ -677,23 +677,42 @@ __global__ __launch_bounds__(kDkvWaves * 64, 2) void thd_bwd_dkdv_kernel(BwdPara
     const uint32_t span = uint32_t(max(hi - lo, 0));
     const int row_bias = 4 * grp - lo;
     const float* info = reinterpret_cast<const float*>(stage + S::INFO);
-    u32x4 ph, pl, dh, dl;
+    // Blocks whose every row sees every key of this wave (all 32 rows real,
+    // the first row at or past the wave's last key) skip the per-element
+    // test; the condition is wave-uniform. Keys past the tile's end only feed
+    // accumulators that are never stored.
+    const int key_hi = ks + wave * kDkvKeysPerWave + kDkvKeysPerWave - 1;
+    const bool whole = b.nrg - b.sb * kRowsPerBlock >= kRowsPerBlock &&
+                       (key_hi - b.qg) * G <= b.sb * kRowsPerBlock;
+    float pr[2][4], d4v[2][4];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
       const int r0 = 16 * rt + 4 * grp;
       const f32x4 l4 = *reinterpret_cast<const f32x4*>(info + r0);
       const f32x4 d4 = *reinterpret_cast<const f32x4*>(info + kRowsPerBlock + r0);
-      float pr[4], ds[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        pr[i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][i], c2, -l4[i]));
-        pr[i] = uint32_t(16 * rt + i + row_bias) < span ? pr[i] : 0.0f;
-        ds[i] = pr[i] * (dp[rt][i] - d4[i]);
+        pr[rt][i] = __builtin_amdgcn_exp2f(__builtin_fmaf(s[rt][i], c2, -l4[i]));
+        d4v[rt][i] = d4[i];
       }
+    }
+    if (!whole) {
+#pragma unroll
+      for (int rt = 0; rt < 2; ++rt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          pr[rt][i] = uint32_t(16 * rt + i + row_bias) < span ? pr[rt][i] : 0.0f;
+    }
+    u32x4 ph, pl, dh, dl;
+#pragma unroll
+    for (int rt = 0; rt < 2; ++rt) {
+      float ds[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) ds[i] = pr[rt][i] * (dp[rt][i] - d4v[rt][i]);
 #pragma unroll
       for (int i = 0; i < 4; i += 2) {
         unsigned hw, lw;
-        split_pair(pr[i], pr[i + 1], hw, lw);
+        split_pair(pr[rt][i], pr[rt][i + 1], hw, lw);
         ph[2 * rt + i / 2] = hw;
         pl[2 * rt + i / 2] = lw;
         split_pair(ds[i], ds[i + 1], hw, lw);
