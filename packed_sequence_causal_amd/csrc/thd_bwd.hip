@@ -680,10 +680,11 @@ __global__ __launch_bounds__(kDkvWaves * 64, 2) void thd_bwd_dkdv_kernel(BwdPara
     // Blocks whose every row sees every key of this wave (all 32 rows real,
     // the first row at or past the wave's last key) skip the per-element
     // test; the condition is wave-uniform. Keys past the tile's end only feed
-    // accumulators that are never stored.
+    // accumulators that are never stored. The clamp keeps the product in
+    // range and changes no outcome: a tile holds fewer than 256 tokens.
     const int key_hi = ks + wave * kDkvKeysPerWave + kDkvKeysPerWave - 1;
     const bool whole = b.nrg - b.sb * kRowsPerBlock >= kRowsPerBlock &&
-                       (key_hi - b.qg) * G <= b.sb * kRowsPerBlock;
+                       min(max(key_hi - b.qg, -1), 256) * G <= b.sb * kRowsPerBlock;
     float pr[2][4], d4v[2][4];
 #pragma unroll
     for (int rt = 0; rt < 2; ++rt) {
