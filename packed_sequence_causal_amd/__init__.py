@@ -6,8 +6,8 @@ the C-ABI library (host planner and HIP kernels). PyTorch supplies device
 memory and the stream. All functions are keyword-only, so that a change of the
 argument list cannot silently shift positional arguments.
 
-The library must have been built in-tree (``python -m
-packed_sequence_causal_amd.build`` or ``__graft_entry__.build()``); importing
+The library must have been built in-tree (``python
+packed_sequence_causal_amd/build.py`` or ``__graft_entry__.build()``); importing
 this package raises if it is missing. There is no fallback path.
 """
 from __future__ import annotations
@@ -58,7 +58,7 @@ def _load():
     if not os.path.exists(LIB_PATH):
         raise ImportError(
             f"{LIB_PATH} is missing: build it first with "
-            "`python -m packed_sequence_causal_amd.build` (no fallback path exists)")
+            "`python packed_sequence_causal_amd/build.py` (no fallback path exists)")
     lib = ctypes.CDLL(LIB_PATH)
     i32, i64, p = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
     pi32 = ctypes.POINTER(ctypes.c_int32)
