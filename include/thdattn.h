@@ -124,10 +124,15 @@ typedef struct {
   int32_t cache_hit;        /* 1 if this handle came from the cache */
 } thd_meta_info_t;
 
-/* Message for the calling thread's last failed call ("" if none). */
+/* Message for the calling thread's last failed call ("" if none). An
+ * interface convention of this library: the pages define no error interface. */
 const char* thd_last_error(void);
 
 /* Symmetric EOD-aware partition of a packed batch for one rank.
+ * Source: "feat: kvallgather cp thd load balance #3820" (Ascend/MindSpeed),
+ * "What this PR does / why we need it?" (EOD-aware symmetric partitioning,
+ * rank-major K/V) and "Does this PR introduce any user-facing change?" (every
+ * subsequence length divisible by 2 * context-parallel size).
  *   seqlens[n_docs]: packed subsequence lengths (host, int32, each >= 1 and
  *   divisible by 2*cp). Writes T and T_local, and any of the host arrays that
  *   are non-NULL: q_global[T_local], kv_row[T], chunk_off[n_docs*2*cp]
@@ -136,7 +141,10 @@ int thd_plan_partition(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32
                        int64_t* total_tokens, int64_t* local_tokens,
                        int32_t* q_global, int32_t* kv_row, int32_t* chunk_off);
 
-/* Build (or fetch from the cache) the metadata of one rank's attention: the
+/* Source: "feat: kvallgather cp thd load balance #3820", "What this PR does /
+ * why we need it?" (metadata cached to avoid recomputing it every call). The
+ * tile tables are this library's own plan for the kernels.
+ * Build (or fetch from the cache) the metadata of one rank's attention: the
  * partition maps, per-tile document/causal bounds for block_t query tokens by
  * block_n keys, the largest-first tile order, the forward work items (see
  * THD_FIELD_ITEMS; concurrency >= 0, 0 = never split a tile) and the backward
@@ -149,7 +157,9 @@ int thd_build_metadata(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32
                        int32_t block_t, int32_t block_n, int32_t concurrency, int32_t device,
                        thd_meta** out);
 
-/* Padding-tolerant partitioning (relaxes the divisibility rule above). A
+/* Padding-tolerant partitioning. It relaxes the divisibility rule of "feat:
+ * kvallgather cp thd load balance #3820", "Does this PR introduce any
+ * user-facing change?", which this library keeps for thd_build_metadata. A
  * document of R_i >= 1 real tokens is stored padded to
  * L_i = ceil(R_i / (2*cp)) * 2*cp tokens: its R_i real tokens first, then
  * L_i - R_i pad tokens (any finite values). The padded batch is partitioned,
@@ -171,27 +181,41 @@ int thd_build_metadata_padded(const int32_t* real_lengths, int32_t n_docs, int32
                               int32_t rank, int32_t block_t, int32_t block_n,
                               int32_t concurrency, int32_t device, thd_meta** out);
 
+/* Sizes and counters of a metadata object (see thd_meta_info_t); the
+ * metadata of "feat: kvallgather cp thd load balance #3820", "What this PR
+ * does / why we need it?". Errors: THD_EINVAL (NULL meta or info). */
 int thd_meta_info(const thd_meta* meta, thd_meta_info_t* info);
 
 /* Copy count int32 values of a field (THD_FIELD_*) into host memory dst;
- * count must equal the field's length. */
+ * count must equal the field's length (THD_EINVAL otherwise, or for an
+ * unknown field or NULL dst). Exposes the cached metadata ("feat:
+ * kvallgather cp thd load balance #3820", "What this PR does / why we need
+ * it?") for bit-exact checks. */
 int thd_meta_copy(const thd_meta* meta, int32_t field, int32_t* dst, int64_t count);
 
-/* Drop one reference (NULL is ignored). */
+/* Drop one reference (NULL is ignored). The entry stays cached until evicted
+ * (least recently used, 64 entries); device memory is freed when the last
+ * reference to an evicted entry goes. */
 void thd_meta_release(thd_meta* meta);
 
-/* Cache counters since the last clear; thd_cache_clear drops every cached
- * entry that no caller still holds. */
+/* Metadata cache ("feat: kvallgather cp thd load balance #3820", "What this
+ * PR does / why we need it?": metadata caching). Counters since the last
+ * clear (any output may be NULL); thd_cache_clear drops every cached entry
+ * that no caller still holds. */
 int thd_cache_stats(int64_t* hits, int64_t* misses, int64_t* uploads, int64_t* entries);
 int thd_cache_clear(void);
 
-/* Tile sizes the kernels expect for a head shape: block_t query tokens per
+/* Head shapes of "feat: kvallgather cp thd load balance #3820", "What this
+ * PR does / why we need it?" (MHA, GQA, expanded MLA).
+ * Tile sizes the kernels expect for a head shape: block_t query tokens per
  * tile and block_n keys per KV tile. THD_EUNSUPPORTED if no kernel exists.
  * These sizes serve the forward and the backward alike. */
 int thd_preferred_tiles(int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
                         int32_t* block_t, int32_t* block_n);
 
-/* Tile sizes for the forward of one batch (seqlens[n_docs] as laid out, i.e.
+/* The tile choice of this library for the forward of "feat: kvallgather cp
+ * thd load balance #3820" (single fused attention call, causal with EOD
+ * reset). Tile sizes for the forward of one batch (seqlens[n_docs] as laid out, i.e.
  * padded lengths for the padded layout; host). The forward also has 32-key
  * tile kernels for d_qk <= 128, run three workgroups per CU instead of two.
  * They are chosen (block_n = 32) when they compute at least 7% fewer key
@@ -205,7 +229,9 @@ int thd_preferred_fwd_tiles(const int32_t* seqlens, int32_t n_docs, int32_t cp, 
                             int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v, int32_t* block_t,
                             int32_t* block_n);
 
-/* Forward work items of one kv head to plan for on a device: its CUs times
+/* Scheduling input of this library's planner (no page passage; it balances
+ * the single fused forward call of "feat: kvallgather cp thd load balance
+ * #3820" over the device). Forward work items of one kv head to plan for on a device: its CUs times
  * the forward workgroups per CU for this KV tile size (2 for block_n = 64, 3
  * for 32), times 7/8, over hkv (at least 1). The 7/8 leaves the split parts
  * slightly longer, which measured faster than filling every slot. Pass it as
@@ -214,14 +240,19 @@ int thd_preferred_fwd_tiles(const int32_t* seqlens, int32_t n_docs, int32_t cp, 
 int thd_fwd_concurrency(int32_t device, int32_t hkv, int32_t block_n, int32_t* concurrency);
 
 /* Bytes of device workspace thd_attn_fwd needs for the partial results of
- * split tiles (0 when no tile is split). */
+ * split tiles (0 when no tile is split). Errors: THD_EINVAL (NULL meta or
+ * bytes, bad head counts, d_v < 1). */
 int thd_attn_fwd_workspace(const thd_meta* meta, int32_t hq, int32_t hkv, int32_t d_v,
                            int64_t* bytes);
 
 /* Forward: o and lse for every local query row and q head.
+ * Source: "feat: kvallgather cp thd load balance #3820", "What this PR does /
+ * why we need it?" (THD attention with direct rank-major K/V indexing in a
+ * single fused call; MHA, GQA, expanded MLA) and "Does this PR introduce any
+ * user-facing change?" (causal attention with the mask reset at every EOD).
  * meta must come from thd_build_metadata with the tile sizes of
- * thd_preferred_tiles or thd_preferred_fwd_tiles and the current device. softmax_scale > 0 (callers
- * usually pass 1/sqrt(d_qk)). Supported (d_qk, d_v): (64,64), (128,128),
+ * thd_preferred_tiles or thd_preferred_fwd_tiles and the current device.
+ * softmax_scale >= 0 and finite; 0 selects 1/sqrt(d_qk). Supported (d_qk, d_v): (64,64), (128,128),
  * (192,128); Hq/Hkv <= 128. q, k, v, o, lse must be 16-byte aligned; k and v
  * must each be smaller than 4 GiB (THD_ERANGE otherwise). workspace (16-byte
  * aligned, at least thd_attn_fwd_workspace bytes; may be NULL when that is 0)
@@ -236,10 +267,18 @@ int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void*
                  int32_t d_v, float softmax_scale, void* workspace, int64_t workspace_bytes,
                  void* hip_stream);
 
-/* Bytes of device workspace thd_attn_bwd needs (caller allocates). */
+/* Bytes of device workspace thd_attn_bwd needs (caller allocates): D and
+ * the base-2 log-sum-exp, two fp32 [T_local, Hq] arrays. Errors: THD_EINVAL. */
 int thd_attn_bwd_workspace(const thd_meta* meta, int32_t hq, int64_t* bytes);
 
-/* Backward: dq, and this rank's partial dk, dv (all fp32, layouts above),
+/* Backward of thd_attn_fwd. The pages give no backward formula; the
+ * gradients are those of the forward's definition, and dk, dv in the gathered
+ * layout are what the all-gather's backward (a reduce-scatter over the ranks;
+ * "[Optim] FlashMask-4 Overlap support part 1 (NVSHMEM backend) - #166",
+ * feature list: reduce-scatter in the backward) sums to their owners.
+ * softmax_scale as for thd_attn_fwd (0 selects 1/sqrt(d_qk)); same head
+ * dims, alignment and size limits; metadata with block_n = 64.
+ * Backward: dq, and this rank's partial dk, dv (all fp32, layouts above),
  * from the forward's lse and the upstream gradient d_o. dk and dv are written
  * in full (zeros for keys no local query sees). The softmax-gradient term
  * D = rowsum(dO * O) needs O exact: it is taken from o_f32 (the forward's

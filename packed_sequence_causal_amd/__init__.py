@@ -13,7 +13,6 @@ this package raises if it is missing. There is no fallback path.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 
 import numpy as np
@@ -265,7 +264,8 @@ _CONCURRENCY = {}
 def preferred_fwd_tiles(*, seqlens, cp: int, rank: int, hq: int, hkv: int, d_qk: int, d_v: int,
                         padded: bool = False) -> tuple[int, int]:
     """Forward tile sizes for this batch (thd_preferred_fwd_tiles): 32-key
-    tiles when no query tile sees more than 512 keys and d_qk <= 128."""
+    tiles when d_qk <= 128 and they compute at least 7% fewer key slots than
+    64-key tiles (query tiles visit whole KV tiles up to their last row)."""
     lens = pad_lengths(seqlens=seqlens, cp=cp) if padded else _lengths(seqlens)
     bt, bn = ctypes.c_int32(), ctypes.c_int32()
     _check(_lib.thd_preferred_fwd_tiles(_ptr32(lens), len(lens), cp, rank, hq, hkv, d_qk, d_v,
@@ -314,48 +314,76 @@ def _scratch(device, nbytes: int, stream):
     return buf
 
 
+def _need(name, t, dtype, shape, dev):
+    """Raise ThdError unless t is a contiguous tensor of this dtype, shape and
+    device: the kernels size every load and store from the head counts and
+    dims, so a mismatched tensor must be refused before the launch."""
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise ThdError(-1, f"{name} must be a torch tensor")
+    if t.dtype != dtype:
+        raise ThdError(-1, f"{name} must be {dtype}, not {t.dtype}")
+    if t.device != dev:
+        raise ThdError(-1, f"{name} is on {t.device}, the call runs on {dev}")
+    if not t.is_contiguous():
+        raise ThdError(-1, f"{name} must be contiguous")
+    if tuple(t.shape) != tuple(shape):
+        raise ThdError(-5, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _qkv_shapes(q, k, v):
+    """Head counts and dims from q, k, v (checked: 3-d bf16 device tensors)."""
+    torch = _torch()
+    for name, t in (("q", q), ("k", k), ("v", v)):
+        if not isinstance(t, torch.Tensor) or t.dim() != 3 or t.dtype != torch.bfloat16 \
+                or not t.is_cuda:
+            raise ThdError(-1, f"{name} must be a 3-d bf16 device tensor")
+    return q.shape[1], k.shape[1], q.shape[2], v.shape[2]
+
+
 def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=None, lse=None,
              out_f32=None, stream=None, meta: Meta | None = None, concurrency: int | None = None,
              padded: bool = False):
     """Forward attention for one rank. Returns (o bf16 [T_loc,Hq,dv], lse fp32 [T_loc,Hq]).
 
     q [T_loc, Hq, dqk], k [T, Hkv, dqk], v [T, Hkv, dv]: bf16 CUDA tensors,
-    k/v already gathered rank-major. softmax_scale defaults to 1/sqrt(dqk).
-    out_f32 (optional fp32 [T_loc, Hq, dv] tensor) also receives O in fp32,
-    computed with split probabilities: pass it to attn_bwd as o_f32.
+    k/v already gathered rank-major. softmax_scale None lets the library use
+    1/sqrt(dqk). out_f32 (optional fp32 [T_loc, Hq, dv] tensor) also receives O
+    in fp32, computed with split probabilities: pass it to attn_bwd as o_f32.
     padded: seqlens are real lengths and the tensors use the padded layout
     (see build_metadata); pad rows get O = 0 and LSE = +inf.
     """
     torch = _torch()
-    hq, hkv, d_qk, d_v = q.shape[1], k.shape[1], q.shape[2], v.shape[2]
-    for name, t in (("q", q), ("k", k), ("v", v)):
-        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 3:
-            raise ThdError(-1, f"{name} must be a contiguous 3-d bf16 device tensor")
-    device = q.device.index
+    hq, hkv, d_qk, d_v = _qkv_shapes(q, k, v)
+    dev = q.device
     if meta is None:
         meta = device_metadata(seqlens=seqlens, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=d_qk,
-                               d_v=d_v, device=device, concurrency=concurrency, padded=padded,
-                               forward=True)
+                               d_v=d_v, device=dev.index, concurrency=concurrency,
+                               padded=padded, forward=True)
     inf = meta._cached_info()
-    if q.shape[0] != inf["local_tokens"] or k.shape[0] != inf["total_tokens"] \
-            or v.shape[0] != inf["total_tokens"]:
-        raise ThdError(-5, "token counts do not match the lengths")
-    need = meta.fwd_workspace_bytes(hq, hkv, d_v)
-    ws = _scratch(q.device, need, stream)
+    t_loc, total = inf["local_tokens"], inf["total_tokens"]
+    _need("q", q, torch.bfloat16, (t_loc, hq, d_qk), dev)
+    _need("k", k, torch.bfloat16, (total, hkv, d_qk), dev)
+    _need("v", v, torch.bfloat16, (total, hkv, d_v), dev)
     if out is None:
-        out = torch.empty((q.shape[0], hq, d_v), dtype=torch.bfloat16, device=q.device)
+        out = torch.empty((t_loc, hq, d_v), dtype=torch.bfloat16, device=dev)
+    else:
+        _need("out", out, torch.bfloat16, (t_loc, hq, d_v), dev)
     if lse is None:
-        lse = torch.empty((q.shape[0], hq), dtype=torch.float32, device=q.device)
-    scale = 1.0 / math.sqrt(d_qk) if softmax_scale is None else float(softmax_scale)
-    if out_f32 is not None and (out_f32.dtype != torch.float32 or not out_f32.is_contiguous()
-                                or tuple(out_f32.shape) != (q.shape[0], hq, d_v)):
-        raise ThdError(-1, "out_f32 must be a contiguous fp32 [T_local, Hq, d_v] tensor")
+        lse = torch.empty((t_loc, hq), dtype=torch.float32, device=dev)
+    else:
+        _need("lse", lse, torch.float32, (t_loc, hq), dev)
+    if out_f32 is not None:
+        _need("out_f32", out_f32, torch.float32, (t_loc, hq, d_v), dev)
+    need = meta.fwd_workspace_bytes(hq, hkv, d_v)
+    ws = _scratch(dev, need, stream)
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
     _check(_lib.thd_attn_fwd(meta.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                              out.data_ptr(), lse.data_ptr(),
                              None if out_f32 is None else out_f32.data_ptr(),
                              hq, hkv, d_qk, d_v, scale,
                              None if ws is None else ws.data_ptr(), need,
-                             _stream_handle(stream, q.device)))
+                             _stream_handle(stream, dev)))
     return out, lse
 
 
@@ -366,40 +394,44 @@ def attn_bwd(*, q, k, v, lse, d_o, seqlens, cp: int, rank: int, softmax_scale=No
     this rank's partial sums in the gathered layout (zeros for unseen keys).
     lse is the forward's. o_f32 (optional) is the forward's fp32 O from
     attn_fwd(out_f32=...): D then comes from it instead of a pass over the keys.
-    padded: as for attn_fwd; the forward's LSE = +inf on pad rows gives them
-    dQ = 0 and no share in dK, dV, whatever d_o holds there."""
+    workspace (optional): a device tensor of at least the bytes
+    thd_attn_bwd_workspace gives. padded: as for attn_fwd; the forward's
+    LSE = +inf on pad rows gives them dQ = 0 and no share in dK, dV, whatever
+    d_o holds there."""
     torch = _torch()
-    hq, hkv, d_qk, d_v = q.shape[1], k.shape[1], q.shape[2], v.shape[2]
-    device = q.device.index
+    hq, hkv, d_qk, d_v = _qkv_shapes(q, k, v)
+    dev = q.device
     if meta is None or meta._cached_info()["block_n"] != preferred_tiles(
             hq=hq, hkv=hkv, d_qk=d_qk, d_v=d_v)[1]:
         # the backward kernels take the general tile sizes only
         meta = device_metadata(seqlens=seqlens, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=d_qk,
-                               d_v=d_v, device=device, padded=padded)
+                               d_v=d_v, device=dev.index, padded=padded)
     inf = meta._cached_info()
-    if q.shape[0] != inf["local_tokens"] or k.shape[0] != inf["total_tokens"]:
-        raise ThdError(-5, "token counts do not match the lengths")
+    t_loc, total = inf["local_tokens"], inf["total_tokens"]
+    _need("q", q, torch.bfloat16, (t_loc, hq, d_qk), dev)
+    _need("k", k, torch.bfloat16, (total, hkv, d_qk), dev)
+    _need("v", v, torch.bfloat16, (total, hkv, d_v), dev)
+    _need("lse", lse, torch.float32, (t_loc, hq), dev)
+    _need("d_o", d_o, torch.bfloat16, (t_loc, hq, d_v), dev)
+    if o_f32 is not None:
+        _need("o_f32", o_f32, torch.float32, (t_loc, hq, d_v), dev)
     need = ctypes.c_int64()
     _check(_lib.thd_attn_bwd_workspace(meta.handle, hq, ctypes.byref(need)))
     if workspace is None:
-        workspace = _scratch(q.device, need.value, stream)
-    dq = torch.empty(q.shape, dtype=torch.float32, device=q.device)
-    dk = torch.empty(k.shape, dtype=torch.float32, device=q.device)
-    dv = torch.empty(v.shape, dtype=torch.float32, device=q.device)
-    scale = 1.0 / math.sqrt(d_qk) if softmax_scale is None else float(softmax_scale)
-    for name, t in (("q", q), ("k", k), ("v", v), ("d_o", d_o)):
-        if t.dtype != torch.bfloat16 or not t.is_cuda or not t.is_contiguous() or t.dim() != 3:
-            raise ThdError(-1, f"{name} must be a contiguous 3-d bf16 device tensor")
-    if lse.dtype != torch.float32 or not lse.is_contiguous() or tuple(lse.shape) != (q.shape[0], hq):
-        raise ThdError(-1, "lse must be a contiguous fp32 [T_local, Hq] tensor")
-    if tuple(d_o.shape) != (q.shape[0], hq, d_v):
-        raise ThdError(-5, "d_o must be [T_local, Hq, d_v]")
-    if o_f32 is not None and (o_f32.dtype != torch.float32 or not o_f32.is_contiguous()
-                              or tuple(o_f32.shape) != (q.shape[0], hq, d_v)):
-        raise ThdError(-1, "o_f32 must be a contiguous fp32 [T_local, Hq, d_v] tensor")
+        workspace = _scratch(dev, need.value, stream)
+    elif not isinstance(workspace, torch.Tensor) or workspace.device != dev \
+            or not workspace.is_contiguous():
+        raise ThdError(-1, f"workspace must be a contiguous tensor on {dev}")
+    ws_bytes = workspace.numel() * workspace.element_size()
+    if ws_bytes < need.value:
+        raise ThdError(-1, f"workspace has {ws_bytes} bytes, needs {need.value}")
+    dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
     _check(_lib.thd_attn_bwd(meta.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                              lse.data_ptr(), None if o_f32 is None else o_f32.data_ptr(),
                              d_o.data_ptr(), dq.data_ptr(), dk.data_ptr(),
                              dv.data_ptr(), hq, hkv, d_qk, d_v, scale, workspace.data_ptr(),
-                             workspace.numel(), _stream_handle(stream, q.device)))
+                             ws_bytes, _stream_handle(stream, dev)))
     return dq, dk, dv

@@ -156,8 +156,12 @@ void check_heads(int32_t hq, int32_t hkv) {
   if (hq / hkv > kRowsPerWg) fail(THD_EUNSUPPORTED, "hq / hkv must be <= 128");
 }
 
-void check_scale(float scale) {
-  if (!(std::isfinite(scale) && scale > 0.0f)) fail(THD_EINVAL, "softmax_scale must be finite and > 0");
+// softmax_scale = 0 selects the default 1/sqrt(d_qk), the usual scaling of
+// dot-product attention (the subject page gives no scale of its own).
+float resolve_scale(float scale, int32_t d_qk) {
+  if (!(std::isfinite(scale) && scale >= 0.0f))
+    fail(THD_EINVAL, "softmax_scale must be finite and >= 0 (0 = 1/sqrt(d_qk))");
+  return scale == 0.0f ? float(1.0 / std::sqrt(double(d_qk))) : scale;
 }
 
 void check_rows(const Plan& p, int32_t group) {
@@ -480,7 +484,7 @@ int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void*
     if (!fwd_supported(d_qk, d_v))
       fail(THD_EUNSUPPORTED, "no forward kernel for d_qk=" + std::to_string(d_qk) +
                                  ", d_v=" + std::to_string(d_v));
-    check_scale(softmax_scale);
+    softmax_scale = resolve_scale(softmax_scale, d_qk);
     const int32_t group = hq / hkv;
     check_fwd_tiles(p, group, d_qk);
     check_ptr(q, "q", 16);
@@ -548,7 +552,7 @@ int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void*
     if (!bwd_supported(d_qk, d_v))
       fail(THD_EUNSUPPORTED, "no backward kernel for d_qk=" + std::to_string(d_qk) +
                                  ", d_v=" + std::to_string(d_v));
-    check_scale(softmax_scale);
+    softmax_scale = resolve_scale(softmax_scale, d_qk);
     const int32_t group = hq / hkv;
     check_bwd_tiles(p, group);
     check_ptr(q, "q", 16);

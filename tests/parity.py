@@ -25,20 +25,5 @@ def assert_close(got, want, what, max_abs=MAX_ABS, mean_abs=MEAN_ABS):
     return mx, mean
 
 
-def sample_rows(n_rows, q_global, cu, count, seed):
-    """Sampled local rows: first rows, last rows, document starts/ends, random."""
-    rng = np.random.default_rng(seed)
-    pick = set(range(min(8, n_rows))) | set(range(max(0, n_rows - 8), n_rows))
-    starts = set(cu[:-1])
-    ends = {c - 1 for c in cu[1:]}
-    for row, g in enumerate(q_global.tolist()):
-        if g in starts or g in ends or (g + 1) in starts:
-            pick.add(row)
-        if len(pick) > count // 2:
-            break
-    pick |= set(rng.choice(n_rows, size=min(count, n_rows), replace=False).tolist())
-    return np.asarray(sorted(pick), dtype=np.int64)
-
-
 def device():
     return torch.device("cuda", 0)

@@ -1,9 +1,9 @@
 """Forward parity of the HIP path against the fp64 oracle, on an MI355X.
 
-Small cases are compared element by element over every output; the full-size
-workloads are compared on sampled rows the oracle computes one at a time, and
-on properties that hold at any size (document-start rows, EOD isolation,
-causality, determinism, union over ranks).
+Every case, the full-size workloads included, is compared element by element
+over every output; properties that hold at any size are checked besides
+(document-start rows, EOD isolation, causality, determinism, union over
+ranks).
 """
 import numpy as np
 import pytest
@@ -12,7 +12,7 @@ import torch
 import workloads
 from oracle import attention as oatt
 from oracle import partition as opart
-from parity import LSE_ABS, assert_close, device, sample_rows, to64
+from parity import LSE_ABS, assert_close, device, to64
 
 pytestmark = pytest.mark.gpu
 
@@ -194,24 +194,44 @@ def test_forward_custom_scale():
     want_o, want_lse = oatt.attn_fwd64(to64(b.q), to64(b.k), to64(b.v), b.lengths, 2, 1, scale=0.3)
     assert_close(to64(o), want_o, "O")
     assert_close(lse.cpu().double().numpy(), want_lse, "LSE", max_abs=LSE_ABS, mean_abs=LSE_ABS)
+    # the library's default scale is 1/sqrt(d_qk), rounded to fp32
+    o_def, lse_def = _run(b)
+    o_exp, lse_exp = _run(b, scale=float(np.float32(1.0 / np.sqrt(128.0))))
+    assert torch.equal(o_def, o_exp) and torch.equal(lse_def, lse_exp)
 
 
 @pytest.mark.parametrize("w", workloads.WORKLOADS, ids=lambda w: w.name)
-def test_forward_full_size_sampled_rows(w):
+def test_forward_full_size_every_element(w):
+    """Each workload at its full size, in the launch configuration the
+    benchmark times (the forward's tile choice for the batch and the device's
+    split plan): every element of O and LSE against the fp64 oracle."""
     b = workloads.make_batch(w)
-    o, lse = _run(b)
-    qg = opart.q_global(b.lengths, w.cp, w.rank)
-    cu = opart.cu_seqlens(b.lengths)
-    rows = sample_rows(w.t_local, qg, cu, 48, w.index)
-    want_o, want_lse = oatt.attn_fwd64_rows(b.q.float().numpy(), b.k.float().numpy(),
-                                            b.v.float().numpy(), b.lengths, w.cp, w.rank, rows)
-    assert_close(to64(o[torch.from_numpy(rows).to(o.device)]), want_o, f"{w.name} O rows")
-    assert_close(lse[torch.from_numpy(rows).to(o.device)].cpu().double().numpy(), want_lse,
-                 f"{w.name} LSE rows", max_abs=LSE_ABS, mean_abs=LSE_ABS)
-    assert torch.isfinite(o.float()).all().item()
+    dev = device()
+    q, k, v = b.q.to(dev), b.k.to(dev), b.v.to(dev)
+    meta = thd.device_metadata(seqlens=b.lengths, cp=w.cp, rank=w.rank, hq=w.hq, hkv=w.hkv,
+                               d_qk=w.d_qk, d_v=w.d_v, device=0, forward=True)
+    info = meta.info()
+    print(f"[fwd full] {w.name} block_n={info['block_n']} items={info['n_items']} "
+          f"splits={info['n_splits']}", flush=True)
+    # the paths the benchmark runs on these workloads are the ones compared here
+    if w.name == "mla":
+        assert info["n_splits"] > 0          # split key ranges plus the combine pass
+    if w.name == "short":
+        assert info["block_n"] == 32         # the 32-key tile kernel
+    o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=b.lengths, cp=w.cp, rank=w.rank, meta=meta)
+    torch.cuda.synchronize()
+    want_o, want_lse = oatt.attn_fwd64(to64(b.q), to64(b.k), to64(b.v), b.lengths, w.cp, w.rank)
+    mx, mean = assert_close(to64(o), want_o, f"{w.name} O")
+    lmx, _ = assert_close(lse.cpu().double().numpy(), want_lse, f"{w.name} LSE",
+                          max_abs=LSE_ABS, mean_abs=LSE_ABS)
+    print(f"[fwd full] {w.name} O max-abs {mx:.3g} mean-abs {mean:.3g} LSE max-abs {lmx:.3g}",
+          flush=True)
     # rows that are a document's first token see one key: O equals V exactly
     if w.rank == 0:
-        starts = [qg.tolist().index(c) for c in cu[:-1]]
+        qg = opart.q_global(b.lengths, w.cp, w.rank)
+        cu = opart.cu_seqlens(b.lengths)
+        pos = {g: i for i, g in enumerate(qg.tolist())}
+        starts = [pos[c] for c in cu[:-1]]
         rows_v = opart.kv_row(b.lengths, w.cp)[cu[:-1]]
         group = w.hq // w.hkv
         got = o[torch.tensor(starts, device=o.device)].cpu()
@@ -291,3 +311,50 @@ def test_forward_reports_errors_from_device_path():
     assert err.value.status == "THD_EMISMATCH"
     with pytest.raises(thd.ThdError):
         thd.attn_fwd(q=q, k=k[:-2], v=v[:-2], seqlens=b.lengths, cp=2, rank=0)
+
+
+def test_binding_refuses_mismatched_tensors_before_launch():
+    """Every tensor is checked (dtype, device, contiguity, exact shape) before
+    the library is called: the kernels size their loads and stores from the
+    head counts and dims, so a wrong tensor must fail as ThdError, not as a
+    device fault."""
+    b = workloads.small_case(41, [64, 128], 2, 8, 2, 128, 128, backward=True, rank=1)
+    dev = device()
+    q, k, v, do = (t.to(dev) for t in (b.q, b.k, b.v, b.do))
+    kw = dict(seqlens=b.lengths, cp=2, rank=1)
+    t_loc, hq, dv = q.shape[0], q.shape[1], v.shape[2]
+    bad_fwd = [
+        dict(v=v[:, :1].contiguous()),                                 # Hkv of v != Hkv of k
+        dict(k=k[:, :, :64].contiguous()),                             # d_qk of k != d_qk of q
+        dict(v=v[:-2]),                                                # too few K/V rows
+        dict(q=q.transpose(0, 1)),                                     # not contiguous
+        dict(k=k.float()),                                             # wrong dtype
+        dict(out=torch.empty((t_loc, hq, dv - 8), dtype=torch.bfloat16, device=dev)),
+        dict(out=torch.empty((t_loc, hq, dv), dtype=torch.float32, device=dev)),
+        dict(lse=torch.empty((t_loc, hq), dtype=torch.float32)),       # host tensor
+        dict(lse=torch.empty((t_loc, hq + 1), dtype=torch.float32, device=dev)),
+        dict(out_f32=torch.empty((t_loc, hq, dv), dtype=torch.bfloat16, device=dev)),
+    ]
+    for change in bad_fwd:
+        args = dict(q=q, k=k, v=v)
+        args.update(change)
+        with pytest.raises(thd.ThdError):
+            thd.attn_fwd(**args, **kw)
+    o, lse = thd.attn_fwd(q=q, k=k, v=v, **kw)
+    bad_bwd = [
+        dict(v=v[:-2]),
+        dict(v=v[:, :1].contiguous()),
+        dict(lse=lse.cpu()),
+        dict(lse=lse[:-1]),
+        dict(d_o=do[:, :, :64].contiguous()),
+        dict(d_o=do.float()),
+        dict(o_f32=torch.empty((t_loc, hq, dv), dtype=torch.bfloat16, device=dev)),
+        dict(workspace=torch.empty(16, dtype=torch.uint8, device=dev)),   # too small
+        dict(workspace=torch.empty(1 << 20, dtype=torch.uint8)),          # host tensor
+    ]
+    for change in bad_bwd:
+        args = dict(q=q, k=k, v=v, lse=lse, d_o=do)
+        args.update(change)
+        with pytest.raises(thd.ThdError):
+            thd.attn_bwd(**args, **kw)
+    torch.cuda.synchronize()

@@ -238,9 +238,12 @@ def test_forward_rejects_host_only_metadata_and_bad_arguments():
     tail = [None, 0, None]
     # unsupported head dims are refused before any device check
     assert lib.thd_attn_fwd(*args, 32, 8, 96, 96, 0.1, *tail) == -8
-    # bad scale
-    assert lib.thd_attn_fwd(*args, 32, 8, 128, 128, 0.0, *tail) == -1
+    # bad scale (0 selects 1/sqrt(d_qk) and so passes this check)
+    assert lib.thd_attn_fwd(*args, 32, 8, 128, 128, -0.5, *tail) == -1
     assert lib.thd_attn_fwd(*args, 32, 8, 128, 128, float("nan"), *tail) == -1
+    assert lib.thd_attn_fwd(*args, 32, 8, 128, 128, float("inf"), *tail) == -1
+    assert b"softmax_scale" in lib.thd_last_error()
+    assert lib.thd_attn_fwd(*args, 32, 8, 128, 128, 0.0, *tail) == -5
     # tile sizes that do not fit the group size
     assert lib.thd_attn_fwd(*args, 64, 8, 128, 128, 0.1, *tail) == -5
     # misaligned pointer
