@@ -267,6 +267,25 @@ int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void*
                  int32_t d_v, float softmax_scale, void* workspace, int64_t workspace_bytes,
                  void* hip_stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the forward
+ * of thd_attn_fwd with the same arguments, checks and results, minus the
+ * workspace. The split tiles' partial results go to a file-scope device array
+ * of 64 MiB (THD_FWD_NOALLOC_SCRATCH_BYTES), one copy per device, held until
+ * the process ends; its device address is looked up once per device, on the
+ * first call there. The call allocates nothing: the caller passes every input
+ * and output, and the metadata must already be built on this device.
+ * THD_ERANGE when the partial results need more than the array holds
+ * (thd_attn_fwd_workspace gives the need; build the metadata with a smaller
+ * concurrency, or call thd_attn_fwd). Every call on one device shares that
+ * device's array, which keeps the last call's contents (no part of it needs
+ * to start at zero): calls that overlap on one device, on other streams or
+ * threads, race on it and must be serialised by the caller. */
+#define THD_FWD_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int thd_attn_fwd_noalloc(const thd_meta* meta, const void* q, const void* k, const void* v,
+                         void* o, float* lse, float* o_f32, int32_t hq, int32_t hkv,
+                         int32_t d_qk, int32_t d_v, float softmax_scale, void* hip_stream);
+
 /* Bytes of device workspace thd_attn_bwd needs (caller allocates): D and
  * the base-2 log-sum-exp, two fp32 [T_local, Hq] arrays. Errors: THD_EINVAL. */
 int thd_attn_bwd_workspace(const thd_meta* meta, int32_t hq, int64_t* bytes);

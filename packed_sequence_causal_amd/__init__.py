@@ -82,6 +82,8 @@ def _load():
         "thd_attn_fwd_workspace": (ctypes.c_int, [p, i32, i32, i32, pi64]),
         "thd_attn_fwd": (ctypes.c_int, [p, p, p, p, p, p, p, i32, i32, i32, i32, ctypes.c_float, p,
                                         i64, p]),
+        "thd_attn_fwd_noalloc": (ctypes.c_int, [p, p, p, p, p, p, p, i32, i32, i32, i32,
+                                                ctypes.c_float, p]),
         "thd_attn_bwd_workspace": (ctypes.c_int, [p, i32, pi64]),
         "thd_attn_bwd": (ctypes.c_int, [p, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
                                         ctypes.c_float, p, i64, p]),
@@ -98,7 +100,7 @@ EXPORTS = ("thd_last_error", "thd_plan_partition", "thd_build_metadata", "thd_pa
            "thd_build_metadata_padded", "thd_meta_info",
            "thd_meta_copy", "thd_meta_release", "thd_cache_stats", "thd_cache_clear",
            "thd_preferred_tiles", "thd_preferred_fwd_tiles", "thd_fwd_concurrency",
-           "thd_attn_fwd_workspace", "thd_attn_fwd",
+           "thd_attn_fwd_workspace", "thd_attn_fwd", "thd_attn_fwd_noalloc",
            "thd_attn_bwd_workspace", "thd_attn_bwd")
 
 
@@ -384,6 +386,32 @@ def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=No
                              hq, hkv, d_qk, d_v, scale,
                              None if ws is None else ws.data_ptr(), need,
                              _stream_handle(stream, dev)))
+    return out, lse
+
+
+def attn_fwd_noalloc(*, q, k, v, out, lse, meta: Meta, out_f32=None, softmax_scale=None,
+                     stream=None):
+    """thd_attn_fwd_noalloc: the forward into caller-given out and lse with
+    metadata built beforehand; nothing is allocated (the split tiles' partial
+    results use the library's per-device static array). Calls that overlap on
+    one device race on that array."""
+    torch = _torch()
+    hq, hkv, d_qk, d_v = _qkv_shapes(q, k, v)
+    dev = q.device
+    inf = meta._cached_info()
+    t_loc, total = inf["local_tokens"], inf["total_tokens"]
+    _need("q", q, torch.bfloat16, (t_loc, hq, d_qk), dev)
+    _need("k", k, torch.bfloat16, (total, hkv, d_qk), dev)
+    _need("v", v, torch.bfloat16, (total, hkv, d_v), dev)
+    _need("out", out, torch.bfloat16, (t_loc, hq, d_v), dev)
+    _need("lse", lse, torch.float32, (t_loc, hq), dev)
+    if out_f32 is not None:
+        _need("out_f32", out_f32, torch.float32, (t_loc, hq, d_v), dev)
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    _check(_lib.thd_attn_fwd_noalloc(meta.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                     out.data_ptr(), lse.data_ptr(),
+                                     None if out_f32 is None else out_f32.data_ptr(),
+                                     hq, hkv, d_qk, d_v, scale, _stream_handle(stream, dev)))
     return out, lse
 
 

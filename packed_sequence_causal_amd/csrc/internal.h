@@ -113,6 +113,14 @@ THD_HOST_DEVICE inline int64_t fwd_partial_floats(int32_t block_t, int32_t group
   return (int64_t(block_t) * group * (d_v + 1) + 3) / 4 * 4;
 }
 
+// Bytes of the file-scope device array that thd_attn_fwd_noalloc uses as the
+// forward's workspace (one copy per device).
+constexpr int64_t kFwdStaticScratchBytes = THD_FWD_NOALLOC_SCRATCH_BYTES;
+
+// Device address of that array on `device`, which must be the current device;
+// looked up on the first call per device. Returns a hipError_t value.
+int fwd_static_scratch(int device, void** ptr);
+
 // Kernel launchers (defined in the .hip files). Return a hipError_t value.
 int launch_fwd(const FwdParams& p, int d_qk, int d_v, void* stream);
 // Workgroups of the forward kernel for this KV tile size that fit one CU.

@@ -473,61 +473,102 @@ int thd_attn_fwd_workspace(const thd_meta* meta, int32_t hq, int32_t hkv, int32_
   });
 }
 
+}  // extern "C"
+
+namespace thd {
+namespace {
+
+// Shared by thd_attn_fwd (caller workspace) and thd_attn_fwd_noalloc (the
+// per-device static array; use_static = true, workspace ignored).
+void attn_fwd_impl(const thd_meta* meta, const void* q, const void* k, const void* v, void* o,
+                   float* lse, float* o_f32, int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
+                   float softmax_scale, void* workspace, int64_t workspace_bytes, bool use_static,
+                   void* hip_stream) {
+  const MetaEntry& e = entry_of(meta);
+  const Plan& p = *e.plan;
+  check_heads(hq, hkv);
+  if (!fwd_supported(d_qk, d_v))
+    fail(THD_EUNSUPPORTED, "no forward kernel for d_qk=" + std::to_string(d_qk) +
+                               ", d_v=" + std::to_string(d_v));
+  softmax_scale = resolve_scale(softmax_scale, d_qk);
+  const int32_t group = hq / hkv;
+  check_fwd_tiles(p, group, d_qk);
+  check_ptr(q, "q", 16);
+  check_ptr(k, "k", 16);
+  check_ptr(v, "v", 16);
+  check_ptr(o, "o", 16);
+  check_ptr(lse, "lse", 16);
+  if (o_f32 != nullptr) check_ptr(o_f32, "o_f32", 16);
+  const int64_t need = p.n_part_slots * hkv * fwd_partial_floats(p.block_t, group, d_v) *
+                       int64_t(sizeof(float));
+  if (use_static) {
+    if (need > kFwdStaticScratchBytes)
+      fail(THD_ERANGE, "the split tiles' partial results need " + std::to_string(need) +
+                           " bytes; the no-allocation forward holds at most " +
+                           std::to_string(kFwdStaticScratchBytes) +
+                           " (build the metadata with a smaller concurrency, or call "
+                           "thd_attn_fwd with a workspace)");
+  } else if (need > 0) {
+    check_ptr(workspace, "workspace", 16);
+    if (workspace_bytes < need)
+      fail(THD_EINVAL, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
+                           std::to_string(need));
+  }
+  const DeviceMeta& d = device_meta(e);
+  const int64_t n_items = int64_t(p.items.size() / 4);
+  if (n_items * hkv >= (int64_t(1) << 31)) fail(THD_ERANGE, "grid too large");
+  check_kv_bytes(p.total, hkv, d_qk, d_v);
+  if (use_static) {
+    void* ptr = nullptr;
+    check_hip(hipError_t(fwd_static_scratch(d.device, &ptr)), "hipGetSymbolAddress(scratch)");
+    workspace = ptr;
+  }
+  FwdParams fp{};
+  fp.q = q;
+  fp.k = k;
+  fp.v = v;
+  fp.o = o;
+  fp.lse = lse;
+  fp.o_f32 = o_f32;
+  fp.partial = static_cast<float*>(workspace);
+  fp.tiles = d.tiles;
+  fp.items = d.items;
+  fp.splits = d.splits;
+  fp.kv_row = d.kv_row;
+  fp.doc_end = d.doc_end;
+  fp.n_items = int32_t(n_items);
+  fp.n_splits = int32_t(p.splits.size() / 4);
+  fp.hq = hq;
+  fp.hkv = hkv;
+  fp.group = group;
+  fp.block_t = p.block_t;
+  fp.block_n = p.block_n;
+  fp.total = p.total;
+  fp.scale_log2 = softmax_scale * 1.4426950408889634f;
+  check_hip(hipError_t(launch_fwd(fp, d_qk, d_v, hip_stream)), "forward launch");
+}
+
+}  // namespace
+}  // namespace thd
+
+extern "C" {
+
 int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void* v, void* o,
                  float* lse, float* o_f32, int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
                  float softmax_scale, void* workspace, int64_t workspace_bytes,
                  void* hip_stream) {
   return guarded([&] {
-    const MetaEntry& e = entry_of(meta);
-    const Plan& p = *e.plan;
-    check_heads(hq, hkv);
-    if (!fwd_supported(d_qk, d_v))
-      fail(THD_EUNSUPPORTED, "no forward kernel for d_qk=" + std::to_string(d_qk) +
-                                 ", d_v=" + std::to_string(d_v));
-    softmax_scale = resolve_scale(softmax_scale, d_qk);
-    const int32_t group = hq / hkv;
-    check_fwd_tiles(p, group, d_qk);
-    check_ptr(q, "q", 16);
-    check_ptr(k, "k", 16);
-    check_ptr(v, "v", 16);
-    check_ptr(o, "o", 16);
-    check_ptr(lse, "lse", 16);
-    if (o_f32 != nullptr) check_ptr(o_f32, "o_f32", 16);
-    const int64_t need = p.n_part_slots * hkv * fwd_partial_floats(p.block_t, group, d_v) *
-                         int64_t(sizeof(float));
-    if (need > 0) {
-      check_ptr(workspace, "workspace", 16);
-      if (workspace_bytes < need)
-        fail(THD_EINVAL, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
-                             std::to_string(need));
-    }
-    const DeviceMeta& d = device_meta(e);
-    const int64_t n_items = int64_t(p.items.size() / 4);
-    if (n_items * hkv >= (int64_t(1) << 31)) fail(THD_ERANGE, "grid too large");
-    check_kv_bytes(p.total, hkv, d_qk, d_v);
-    FwdParams fp{};
-    fp.q = q;
-    fp.k = k;
-    fp.v = v;
-    fp.o = o;
-    fp.lse = lse;
-    fp.o_f32 = o_f32;
-    fp.partial = static_cast<float*>(workspace);
-    fp.tiles = d.tiles;
-    fp.items = d.items;
-    fp.splits = d.splits;
-    fp.kv_row = d.kv_row;
-    fp.doc_end = d.doc_end;
-    fp.n_items = int32_t(n_items);
-    fp.n_splits = int32_t(p.splits.size() / 4);
-    fp.hq = hq;
-    fp.hkv = hkv;
-    fp.group = group;
-    fp.block_t = p.block_t;
-    fp.block_n = p.block_n;
-    fp.total = p.total;
-    fp.scale_log2 = softmax_scale * 1.4426950408889634f;
-    check_hip(hipError_t(launch_fwd(fp, d_qk, d_v, hip_stream)), "forward launch");
+    attn_fwd_impl(meta, q, k, v, o, lse, o_f32, hq, hkv, d_qk, d_v, softmax_scale, workspace,
+                  workspace_bytes, false, hip_stream);
+  });
+}
+
+int thd_attn_fwd_noalloc(const thd_meta* meta, const void* q, const void* k, const void* v,
+                         void* o, float* lse, float* o_f32, int32_t hq, int32_t hkv,
+                         int32_t d_qk, int32_t d_v, float softmax_scale, void* hip_stream) {
+  return guarded([&] {
+    attn_fwd_impl(meta, q, k, v, o, lse, o_f32, hq, hkv, d_qk, d_v, softmax_scale, nullptr, 0,
+                  true, hip_stream);
   });
 }
 

@@ -43,6 +43,8 @@
 
 #include <climits>
 #include <cstdint>
+#include <mutex>
+#include <vector>
 
 #include "internal.h"
 
@@ -628,7 +630,34 @@ int launch(const FwdParams& p, void* stream) {
   return int(hipGetLastError());
 }
 
+// Workspace of thd_attn_fwd_noalloc: the split tiles' partial results live in
+// this file-scope array instead of a caller's buffer. Each device that runs the
+// library holds its own copy until the process ends. In host code the name
+// only stands for the symbol: kernels get the device address that
+// hipGetSymbolAddress returns for the current device (looked up once per
+// device, on that device's first call).
+static __device__ __align__(256) char scratch[kFwdStaticScratchBytes];
+
+std::mutex g_scratch_mu;
+std::vector<void*> g_scratch_ptr;   // per device id; null until looked up
+
 }  // namespace
+
+int fwd_static_scratch(int device, void** ptr) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (device < 0) return int(hipErrorInvalidDevice);
+  if (size_t(device) >= g_scratch_ptr.size()) g_scratch_ptr.resize(size_t(device) + 1, nullptr);
+  if (g_scratch_ptr[size_t(device)] == nullptr) {
+    // The caller has made `device` current: the address is that device's copy.
+    void* p = nullptr;
+    const hipError_t err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (err != hipSuccess) return int(err);
+    if (p == nullptr) return int(hipErrorInvalidSymbol);
+    g_scratch_ptr[size_t(device)] = p;
+  }
+  *ptr = g_scratch_ptr[size_t(device)];
+  return int(hipSuccess);
+}
 
 bool fwd_supported(int d_qk, int d_v) {
   return (d_qk == 64 && d_v == 64) || (d_qk == 128 && d_v == 128) || (d_qk == 192 && d_v == 128);

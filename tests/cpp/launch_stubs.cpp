@@ -12,4 +12,5 @@ bool fwd_supported(int, int) { return false; }
 bool bwd_supported(int, int) { return false; }
 bool fwd_block_n_supported(int, int) { return false; }
 int fwd_workgroups_per_cu(int) { return 1; }
+int fwd_static_scratch(int, void**) { return int(hipErrorInvalidValue); }
 }  // namespace thd

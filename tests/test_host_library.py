@@ -263,6 +263,32 @@ def test_forward_rejects_host_only_metadata_and_bad_arguments():
     assert b"workspace" in lib.thd_last_error()
 
 
+def test_noalloc_forward_refuses_plans_beyond_its_static_array():
+    """thd_attn_fwd_noalloc checks the split tiles' need against its fixed
+    per-device array before anything touches a device."""
+    lib = thd._lib
+    buf = ctypes.create_string_buffer(1 << 16)
+    ptr = (ctypes.addressof(buf) + 15) // 16 * 16
+    big = thd.build_metadata(seqlens=[65536], cp=1, rank=0, block_t=128, block_n=64,
+                             concurrency=1000)
+    assert big.fwd_workspace_bytes(16, 16, 128) > (64 << 20)
+    assert lib.thd_attn_fwd_noalloc(big.handle, ptr, ptr, ptr, ptr, ptr, None, 16, 16, 128, 128,
+                                    0.0, None) == -3
+    assert b"no-allocation" in lib.thd_last_error()
+    # a plan that fits gets past the size check to the device check (host-only metadata)
+    small = thd.build_metadata(seqlens=[2048, 512, 1024], cp=2, rank=1, block_t=32, block_n=64,
+                               concurrency=64)
+    assert 0 < small.fwd_workspace_bytes(16, 4, 128) <= (64 << 20)
+    assert lib.thd_attn_fwd_noalloc(small.handle, ptr, ptr, ptr, ptr, ptr, None, 16, 4, 128, 128,
+                                    0.0, None) == -5
+    assert b"device" in lib.thd_last_error()
+    # the usual argument checks apply
+    assert lib.thd_attn_fwd_noalloc(small.handle, ptr + 2, ptr, ptr, ptr, ptr, None, 16, 4, 128,
+                                    128, 0.0, None) == -4
+    assert lib.thd_attn_fwd_noalloc(None, ptr, ptr, ptr, ptr, ptr, None, 16, 4, 128, 128, 0.0,
+                                    None) == -1
+
+
 def test_cache_hits_and_key_completeness():
     thd.cache_clear()
     a = thd.build_metadata(seqlens=[8, 16, 8], cp=2, rank=0, block_t=4, block_n=8)
