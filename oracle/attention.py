@@ -166,6 +166,75 @@ def attn_bwd64(q, k, v, do, seqlens, cp, rank, scale=None):
     return dq, dk, dv
 
 
+def attn_fwd64_shards(q, k, v, seqlens, cp, rank, shards, scale=None):
+    """O and LSE over the keys held by the given source ranks' shards (fp64).
+
+    Reading for the all-gather overlap of the FlashMask-4 overlap page
+    ("[Optim] FlashMask-4 Overlap support part 1 (NVSHMEM backend) - #166",
+    feature list, "AG fwd overlap"): the all-gather delivers K/V one source
+    rank's shard at a time, rank s's shard holding chunks s and 2cp-1-s of
+    every document; a forward pass over the shards that have arrived computes
+    the attention of each row restricted to the keys of those shards. With
+    every shard it is attn_fwd64. A row that sees no key of the set gets
+    O = 0 and LSE = -inf (the log of an empty sum).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    lengths, group = _check(q, k, v, seqlens, cp, rank)
+    shards = {int(x) for x in shards}
+    kg = to_global(np.asarray(k, dtype=np.float64), lengths, cp)
+    vg = to_global(np.asarray(v, dtype=np.float64), lengths, cp)
+    if scale is None:
+        scale = 1.0 / math.sqrt(q.shape[2])
+    tl, hq = q.shape[0], q.shape[1]
+    out = np.zeros((tl, hq, v.shape[2]))
+    lse = np.full((tl, hq), -np.inf)
+    for lstart, gstart, c, doc_start, chunk in _segments(lengths, cp, rank):
+        n_keys = (chunk + 1) * c
+        visible = np.arange(n_keys)[None, :] <= (chunk * c + np.arange(c))[:, None]
+        # key j of the document lies in chunk j // c, owned by rank min(k, 2cp-1-k)
+        owner = np.minimum(np.arange(n_keys) // c, 2 * cp - 1 - np.arange(n_keys) // c)
+        held = np.isin(owner, sorted(shards))
+        visible = visible & held[None, :]
+        seen = visible.any(axis=1)
+        if not seen.any():
+            continue
+        for hk in range(k.shape[1]):
+            keys = kg[doc_start:doc_start + n_keys, hk]
+            vals = vg[doc_start:doc_start + n_keys, hk]
+            for h in range(hk * group, (hk + 1) * group):
+                s = scale * (q[lstart:lstart + c, h] @ keys.T)
+                s = np.where(visible, s, -np.inf)[seen]
+                m = s.max(axis=1, keepdims=True)
+                p = np.exp(s - m)
+                denom = p.sum(axis=1, keepdims=True)
+                rows = lstart + np.nonzero(seen)[0]
+                out[rows, h] = (p @ vals) / denom
+                lse[rows, h] = (m + np.log(denom))[:, 0]
+    return out, lse
+
+
+def merge_lse(parts):
+    """Merge partial softmax results over disjoint key sets (fp64).
+
+    parts: (O_i, LSE_i) pairs, each the attention over its own key set. The
+    softmax over the union weights each part by exp(LSE_i - LSE) with
+    LSE = ln sum_i exp(LSE_i); parts with LSE = -inf weigh nothing, and a row
+    no part covers stays O = 0, LSE = -inf.
+    """
+    lses = np.stack([np.asarray(l, dtype=np.float64) for _, l in parts])
+    m = lses.max(axis=0)
+    finite = np.isfinite(m)
+    m_safe = np.where(finite, m, 0.0)
+    w = np.exp(lses - m_safe[None])
+    total = w.sum(axis=0)
+    lse = np.where(finite, m_safe + np.log(np.where(finite, total, 1.0)), -np.inf)
+    out = np.zeros_like(np.asarray(parts[0][0], dtype=np.float64))
+    for (o, _), wi in zip(parts, w):
+        out += wi[..., None] * np.asarray(o, dtype=np.float64)
+    out = np.where(finite[..., None], out / np.where(finite, total, 1.0)[..., None], 0.0)
+    return out, lse
+
+
 def attn_fwd64_padded(q, k, v, real_lengths, cp, rank, scale=None):
     """Forward over the padded layout of partition.pad_lengths (fp64).
 

@@ -55,6 +55,25 @@ kvtiles[m][8] (backward): for document i, j = 0 .. ceil(L_i / BN) - 1:
 The key tiles cover every key once. Keys of document i at offset >=
 (2cp-r)*c_i are seen by no local query (the rank's later chunk is 2cp-1-r), so
 tiles made only of such keys get the empty range q_begin = q_end.
+
+Pass plans (all-gather overlap; a reading of "[Optim] FlashMask-4 Overlap
+support part 1 (NVSHMEM backend) - #166", feature list, "AG fwd overlap"): a
+forward pass over the keys of a set S of source ranks' shards. For each tile
+(same tiles as above; document i, chunk k of its rows, q_glob, n_rows), the
+chunks 0..k the rows can see are grouped into maximal runs [a, b] of
+consecutive chunks whose owner min(chunk, 2cp-1-chunk) is in S. Run [a, b]
+gives the work item
+    lo     = cu_i + a*c_i
+    hi     = cu_i + (b+1)*c_i if b < k else q_glob + n_rows
+    n_kv   = ceil((hi - lo) / BN)            (KV tiles from lo)
+    n_full = min((q_glob - lo + 1) // BN, (hi - lo) // BN)
+    record = [tile, lo, hi, part slot, n_kv, n_full, 0, 0]
+with part slots counted up over the runs in tile order. pass_items lists the
+records sorted by n_kv descending (ties by that listing; parity unpinned);
+pass_tiles[n_tiles][4] = [tile, first part slot, number of runs, 0] for every
+tile in natural order (a tile with no run has 0). Every key of a run lies in a
+chunk the rows see from its start, so every row sees the first key of each of
+its items.
 """
 from __future__ import annotations
 
@@ -180,3 +199,45 @@ def items_and_splits(tile_table: np.ndarray, concurrency: int):
     ranked = sorted(range(len(natural)), key=lambda i: (-(natural[i][2] - natural[i][1]), i))
     items = np.asarray([natural[i] for i in ranked], dtype=np.int32).reshape(-1, 4)
     return items, np.asarray(splits, dtype=np.int32).reshape(-1, 4)
+
+
+def owner(chunk: int, cp: int) -> int:
+    """Source rank whose shard holds a document's chunk (ranks own r, 2cp-1-r)."""
+    return min(chunk, 2 * cp - 1 - chunk)
+
+
+def pass_plan(seqlens, cp: int, rank: int, block_t: int, block_n: int, shards):
+    """(pass_items [n][8] in work order, pass_tiles [n_tiles][4]) for the set of
+    source ranks ``shards`` (see the module docstring)."""
+    lengths = partition.validate(seqlens, cp, rank)
+    held = {int(x) for x in shards}
+    cu = partition.cu_seqlens(lengths)
+    tt = tiles(lengths, cp, rank, block_t, block_n)
+    natural = []
+    table = []
+    slot = 0
+    for t in range(tt.shape[0]):
+        q_glob, n_rows, i, s = (int(x) for x in tt[t, 1:5])
+        c = lengths[i] // (2 * cp)
+        k = rank if s == 0 else 2 * cp - 1 - rank
+        first = slot
+        chunk = 0
+        while chunk <= k:
+            if owner(chunk, cp) not in held:
+                chunk += 1
+                continue
+            a = chunk
+            while chunk + 1 <= k and owner(chunk + 1, cp) in held:
+                chunk += 1
+            b = chunk
+            lo = cu[i] + a * c
+            hi = cu[i] + (b + 1) * c if b < k else q_glob + n_rows
+            n_kv = _ceil_div(hi - lo, block_n)
+            n_full = min((q_glob - lo + 1) // block_n, (hi - lo) // block_n)
+            natural.append([t, lo, hi, slot, n_kv, n_full, 0, 0])
+            slot += 1
+            chunk += 1
+        table.append([t, first, slot - first, 0])
+    ranked = sorted(range(len(natural)), key=lambda j: (-natural[j][4], j))
+    items = np.asarray([natural[j] for j in ranked], dtype=np.int32).reshape(-1, 8)
+    return items, np.asarray(table, dtype=np.int32).reshape(-1, 4)

@@ -337,3 +337,82 @@ def test_padding_without_pads_is_the_plain_oracle():
     o, lse = attention.attn_fwd64_padded(q, k, v, real, cp, rank)
     o2, lse2 = attention.attn_fwd64(q, k, v, real, cp, rank)
     assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+
+
+# --- attention over a subset of source ranks' shards (all-gather overlap) ---
+
+def _library_shards(q_loc, k, v, lengths, cp, rank, shards, scale):
+    """SDPA(float64) and a torch log-sum-exp over the unpartitioned sequence,
+    with the causal + EOD mask narrowed to keys whose gathered row lies in a
+    listed rank's block of the rank-major K/V (row // T_local = holding rank).
+    Returns O, LSE and the rank's rows that see at least one key."""
+    total = int(sum(lengths))
+    t_loc = total // cp
+    qg = partition.q_global(lengths, cp, rank)
+    kg = attention.to_global(k, lengths, cp)
+    vg = attention.to_global(v, lengths, cp)
+    holder = partition.kv_row(lengths, cp) // t_loc          # rank holding each global key
+    q_full = np.random.default_rng(998).standard_normal((total,) + q_loc.shape[1:])
+    q_full[qg] = q_loc
+    docs = partition.doc_of(lengths)
+    idx = np.arange(total)
+    mask = (docs[:, None] == docs[None, :]) & (idx[None, :] <= idx[:, None])
+    mask &= np.isin(holder, list(shards))[None, :]
+    seen = mask[qg].any(axis=1)
+    group = q_loc.shape[1] // k.shape[1]
+    qt = torch.from_numpy(q_full).permute(1, 0, 2)
+    kt = torch.from_numpy(kg).repeat_interleave(group, dim=1).permute(1, 0, 2)
+    vt = torch.from_numpy(vg).repeat_interleave(group, dim=1).permute(1, 0, 2)
+    mt = torch.from_numpy(mask)
+    out = torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, attn_mask=mt, scale=scale)
+    s = (qt @ kt.transpose(1, 2)) * scale
+    lse = torch.logsumexp(s.masked_fill(~mt, float("-inf")), dim=-1)
+    return out.permute(1, 0, 2).numpy()[qg], lse.permute(1, 0).numpy()[qg], seen
+
+
+@pytest.mark.parametrize("lengths,cp,rank,shards", [
+    ([16, 32, 16], 2, 0, {1}),
+    ([16, 32, 16], 2, 1, {0}),
+    ([48, 16, 96, 32], 4, 2, {2}),
+    ([48, 16, 96, 32], 4, 2, {0, 3}),
+    ([48, 16, 96, 32], 4, 1, {1, 2, 3}),
+    ([80, 240], 8, 5, {0, 5, 7}),
+])
+def test_shard_subset_oracle_matches_library(lengths, cp, rank, shards):
+    """Attention restricted to some shards against SDPA with the narrowed mask
+    (holder taken from the rank-major gathered row, not from the chunk formula)."""
+    q, k, v, _ = _case(41, lengths, cp, rank, 4, 2, 12, 8)
+    scale = 0.29
+    o, lse = attention.attn_fwd64_shards(q, k, v, lengths, cp, rank, shards, scale=scale)
+    ref_o, ref_lse, seen = _library_shards(q, k, v, lengths, cp, rank, shards, scale)
+    assert seen.any()
+    assert np.max(np.abs(o[seen] - ref_o[seen])) <= 1e-12
+    assert np.max(np.abs(lse[seen] - ref_lse[seen])) <= 1e-12
+    # rows that see none of the shards' keys: empty softmax
+    assert np.all(o[~seen] == 0.0) and np.all(np.isneginf(lse[~seen]))
+
+
+def test_shard_passes_merge_to_full_attention():
+    """One pass per shard, merged by log-sum-exp weights, is the whole forward;
+    so is the pass over every shard at once. For rank r the rows of chunk r see
+    no key of a shard s > r (its chunks s and 2cp-1-s both follow chunk r)."""
+    lengths, cp, rank = [32, 64, 16, 48], 4, 1
+    q, k, v, _ = _case(42, lengths, cp, rank, 4, 2, 8, 8)
+    full_o, full_lse = attention.attn_fwd64(q, k, v, lengths, cp, rank)
+    all_o, all_lse = attention.attn_fwd64_shards(q, k, v, lengths, cp, rank, range(cp))
+    assert np.max(np.abs(all_o - full_o)) <= 1e-12 and np.max(np.abs(all_lse - full_lse)) <= 1e-12
+    parts = [attention.attn_fwd64_shards(q, k, v, lengths, cp, rank, [s]) for s in range(cp)]
+    m_o, m_lse = attention.merge_lse(parts)
+    assert np.max(np.abs(m_o - full_o)) <= 1e-12 and np.max(np.abs(m_lse - full_lse)) <= 1e-12
+    # merging in another grouping gives the same result
+    m2 = attention.merge_lse([attention.merge_lse(parts[:2]), attention.merge_lse(parts[2:])])
+    assert np.max(np.abs(m2[0] - full_o)) <= 1e-12
+    chunk_r_rows = []
+    cu = partition.cu_seqlens(lengths)
+    qg = partition.q_global(lengths, cp, rank)
+    for i, L in enumerate(lengths):
+        c = L // (2 * cp)
+        chunk_r_rows += [row for row, g in enumerate(qg.tolist())
+                         if cu[i] + rank * c <= g < cu[i] + (rank + 1) * c]
+    for s in range(rank + 1, cp):
+        assert np.all(np.isneginf(parts[s][1][chunk_r_rows]))

@@ -223,3 +223,60 @@ def test_pad_rows_are_the_tokens_past_each_real_end():
     ends = metadata.doc_end(lengths, cp, real)
     assert ends.tolist() == [cu[i] + real[i] for i in range(len(real))]
     assert metadata.doc_end(lengths, cp).tolist() == cu[1:]
+
+
+def test_pass_plans_match_hand_derived_fixture():
+    g = read_records("pass_plan_small.txt")
+    cases = {"A": ([16, 32, 16], 2, 0, 4, 4, [1]), "B": ([16], 2, 1, 2, 2, [0, 1]),
+             "C": ([16], 2, 1, 2, 2, [0])}
+    for name, (lengths, cp, rank, bt, bn, shards) in cases.items():
+        items, table = metadata.pass_plan(lengths, cp, rank, bt, bn, shards)
+        assert items.tolist() == g["item" + name], name
+        assert table.tolist() == g["tile" + name], name
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_pass_plan_covers_each_visible_pair_of_the_shards_once(seed):
+    """Brute force: every (local row, key) pair the causal + EOD mask leaves
+    open and whose key lies in a listed shard is covered by exactly one KV tile
+    of exactly one item; no item reaches a key outside the listed shards; the
+    first n_full KV tiles of an item are wholly visible to all of its rows and
+    every row sees the first key of each of its items."""
+    rng = np.random.default_rng(300 + seed)
+    cp = int(rng.choice([1, 2, 3, 4]))
+    rank = int(rng.integers(0, cp))
+    lengths = [2 * cp * int(x) for x in rng.integers(1, 7, size=int(rng.integers(1, 5)))]
+    bt, bn = int(rng.choice([1, 2, 3, 5])), int(rng.choice([1, 2, 3, 4, 8]))
+    shards = sorted({int(x) for x in rng.integers(0, cp, size=int(rng.integers(1, cp + 1)))})
+    items, table = metadata.pass_plan(lengths, cp, rank, bt, bn, shards)
+    tt = metadata.tiles(lengths, cp, rank, bt, bn)
+    holder = partition.kv_row(lengths, cp) // (sum(lengths) // cp)
+    cu = partition.cu_seqlens(lengths)
+    docs = partition.doc_of(lengths)
+    covered = {}
+    for tile, lo, hi, slot, n_kv, n_full, _, _ in items.tolist():
+        q_glob, n_rows = int(tt[tile, 1]), int(tt[tile, 2])
+        assert n_kv == -(-(hi - lo) // bn) and 0 <= n_full <= n_kv
+        for row_pos in range(q_glob, q_glob + n_rows):
+            assert lo <= row_pos    # every row sees the item's first key
+        for j in range(n_kv):
+            for key in range(lo + j * bn, min(lo + (j + 1) * bn, hi)):
+                assert int(holder[key]) in shards
+                for row_pos in range(q_glob, q_glob + n_rows):
+                    if j < n_full:
+                        assert key <= row_pos
+                    if key <= row_pos:
+                        covered[(row_pos, key)] = covered.get((row_pos, key), 0) + 1
+    want = set()
+    for row_pos in partition.q_global(lengths, cp, rank).tolist():
+        start = cu[int(docs[row_pos])]
+        for key in range(start, row_pos + 1):
+            if int(holder[key]) in shards:
+                want.add((row_pos, key))
+    assert set(covered) == want and all(c == 1 for c in covered.values())
+    # the per-tile table lists each tile's part slots
+    slots = sorted(int(x) for x in items[:, 3]) if items.size else []
+    assert slots == list(range(len(slots)))
+    for tile, first, n_parts, _ in table.tolist():
+        mine = sorted(int(s) for t, _, _, s, *_ in items.tolist() if t == tile)
+        assert mine == list(range(first, first + n_parts))
