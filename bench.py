@@ -285,6 +285,41 @@ def measure(w, args, dev, cpu_budget_s: float):
     else:
         kern_ms = gpu_ms
 
+    # All-gather overlap: the same forward as cp passes, one per source rank's
+    # shard, local shard first (K/V resident): what splitting the forward into
+    # shard passes costs against the one-pass time, and the share of the work
+    # the local shard's pass does before any remote shard is needed.
+    ag = None
+    if not w.backward:
+        bt = thd.preferred_tiles(hq=w.hq, hkv=w.hkv, d_qk=w.d_qk, d_v=w.d_v)[0]
+        order = [w.rank] + [s_ for s_ in range(w.cp) if s_ != w.rank]
+        metas = [thd.build_pass_metadata(seqlens=batch.lengths, cp=w.cp, rank=w.rank, block_t=bt,
+                                         block_n=64, shards=[s_], device=dev.index)
+                 for s_ in order]
+        state = thd.pass_state(meta=metas[0], hq=w.hq, hkv=w.hkv, d_v=w.d_v, device=dev)
+
+        def passes(upto=None):
+            ms = metas if upto is None else metas[:upto]
+            for i, m in enumerate(ms):
+                thd.attn_fwd_pass(q=q, k=k, v=v, meta=m, state=state, first=i == 0,
+                                  last=i == len(metas) - 1, out=o, lse=lse, stream=stream)
+
+        def timed(fn, n=20):
+            for _ in range(3):
+                fn()
+            a0, a1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a0.record(stream)
+            for _ in range(n):
+                fn()
+            a1.record(stream)
+            a1.synchronize()
+            return a0.elapsed_time(a1) / n
+
+        all_ms = timed(passes)
+        local_ms = timed(lambda: passes(1))
+        ag = {"passes": w.cp, "all_passes_ms": round(all_ms, 5), "one_pass_ms": round(kern_ms, 5),
+              "overhead": round(all_ms / kern_ms, 4), "local_pass_ms": round(local_ms, 5)}
+
     # Algorithmic bytes per launch: Q once, every K/V row some local query sees
     # once (keys of document i up to the end of chunk 2cp-1-r), O (bf16, plus
     # the fp32 copy the training forward writes for the backward) and LSE once.
@@ -327,6 +362,8 @@ def measure(w, args, dev, cpu_budget_s: float):
         "metadata": {"build_ms_cold": round(build_ms, 3), "lookup_us_warm": round(lookup_us, 2)},
         "parity": parity,
     }
+    if ag is not None:
+        rec["ag_overlap"] = ag
     if not args.no_cpu_baseline:
         rec["cpu_baseline"] = _cpu_baseline(w, batch, cpu_budget_s)
     return rec
@@ -388,7 +425,7 @@ def main(argv=None) -> int:
         "data": "synthetic",
     }
     for key in ("config", "pct_of_bf16_peak", "roofline", "gpu_ms_per_step", "timing", "metadata",
-                "parity", "cpu_baseline"):
+                "parity", "ag_overlap", "cpu_baseline"):
         if key in head:
             result[key] = head[key]
     result["host"] = {"cpu_model": _cpu_model(), "cpus": len(os.sched_getaffinity(0))}

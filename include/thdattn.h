@@ -122,6 +122,9 @@ typedef struct {
   int32_t n_docs, cp, rank, block_t, block_n, version;
   int32_t device;           /* device holding the uploaded copy, -1 = host only */
   int32_t cache_hit;        /* 1 if this handle came from the cache */
+  int32_t is_pass;          /* 1 for a pass plan (thd_build_pass_metadata) */
+  int32_t item_ints;        /* ints per ITEMS record: 4, or 8 for a pass plan */
+  uint64_t shard_mask;      /* pass plans: bit s set = keys of rank s's shard */
 } thd_meta_info_t;
 
 /* Message for the calling thread's last failed call ("" if none). An
@@ -285,6 +288,56 @@ int thd_attn_fwd(const thd_meta* meta, const void* q, const void* k, const void*
 int thd_attn_fwd_noalloc(const thd_meta* meta, const void* q, const void* k, const void* v,
                          void* o, float* lse, float* o_f32, int32_t hq, int32_t hkv,
                          int32_t d_qk, int32_t d_v, float softmax_scale, void* hip_stream);
+
+/* All-gather overlap, shard by shard. Source: "[Optim] FlashMask-4 Overlap
+ * support part 1 (NVSHMEM backend) - #166" (PaddlePaddle/flash-attention),
+ * feature list: the forward overlapped with the K/V all-gather. Here without
+ * any in-kernel waiting: the all-gather of "feat: kvallgather cp thd load
+ * balance #3820" delivers rank s's shard (its chunks s and 2cp-1-s of every
+ * document, rows [s*T_local, (s+1)*T_local) of the gathered K/V) as a unit, and
+ * the caller runs one forward pass per delivered shard (or set of shards), on
+ * a stream that waits for the delivery (an event). Passes merge into a running
+ * state; the last one writes o and lse, equal to thd_attn_fwd's up to the
+ * order of summation.
+ *
+ * thd_build_pass_metadata: the metadata of a pass over the keys of the source
+ * ranks in shard_mask (bit s = rank s; at least one bit, none at or above cp;
+ * cp <= 64). Same arguments and cache as thd_build_metadata (the mask is part
+ * of the key); block_n must be 64. Its TILES are thd_build_metadata's; ITEMS
+ * are 8 ints per work item, [tile, first key, end key (exclusive), part slot,
+ * KV tiles, KV tiles every row sees whole, 0, 0], one per maximal run of
+ * consecutive chunks the tile's rows see that a listed rank holds, longest
+ * first; SPLITS holds [tile, first part slot, parts, 0] for every tile.
+ * Errors as thd_build_metadata, plus THD_EINVAL (bad mask), THD_ERANGE (cp > 64). */
+int thd_build_pass_metadata(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank,
+                            int32_t block_t, int32_t block_n, uint64_t shard_mask,
+                            int32_t device, thd_meta** out);
+
+/* Bytes a pass needs: parts_bytes of workspace (partial results of its work
+ * items; may be NULL) and state_bytes of running state (fp32 O
+ * [T_local, Hq, d_v] then its base-2 log-sum-exp [T_local, Hq]; may be NULL).
+ * The state is the caller's and lives across the passes of one forward.
+ * Errors: THD_EINVAL, THD_EMISMATCH (not a pass plan). */
+int thd_attn_fwd_pass_workspace(const thd_meta* meta, int32_t hq, int32_t hkv, int32_t d_v,
+                                int64_t* parts_bytes, int64_t* state_bytes);
+
+#define THD_PASS_FIRST 1   /* the state holds nothing yet (its contents are ignored) */
+#define THD_PASS_LAST 2    /* write o and lse instead of the state */
+
+/* One pass: attention of every local row over the keys of the pass's shards,
+ * merged (log-sum-exp weights) into the state; with THD_PASS_LAST the merged
+ * result is written to o (bf16) and lse (natural log) instead. Rows that saw
+ * no key in any pass so far hold an empty state (lse -inf; written as O = 0,
+ * LSE = -inf by a last pass). Arguments and layouts as thd_attn_fwd (o and lse
+ * may be NULL unless THD_PASS_LAST); state (16-byte aligned, state_bytes of
+ * thd_attn_fwd_pass_workspace); workspace (16-byte aligned, parts_bytes).
+ * Every key a pass reads lies in its shards' rows of k and v, so the other
+ * rows may still be in flight. Errors as thd_attn_fwd, plus THD_EMISMATCH
+ * (metadata not a pass plan) and THD_EINVAL (unknown flags). */
+int thd_attn_fwd_pass(const thd_meta* meta, const void* q, const void* k, const void* v,
+                      void* o, float* lse, float* state, int32_t flags, int32_t hq,
+                      int32_t hkv, int32_t d_qk, int32_t d_v, float softmax_scale,
+                      void* workspace, int64_t workspace_bytes, void* hip_stream);
 
 /* Bytes of device workspace thd_attn_bwd needs (caller allocates): D and
  * the base-2 log-sum-exp, two fp32 [T_local, Hq] arrays. Errors: THD_EINVAL. */

@@ -50,6 +50,8 @@ class _Info(ctypes.Structure):
         ("n_docs", ctypes.c_int32), ("cp", ctypes.c_int32), ("rank", ctypes.c_int32),
         ("block_t", ctypes.c_int32), ("block_n", ctypes.c_int32), ("version", ctypes.c_int32),
         ("device", ctypes.c_int32), ("cache_hit", ctypes.c_int32),
+        ("is_pass", ctypes.c_int32), ("item_ints", ctypes.c_int32),
+        ("shard_mask", ctypes.c_uint64),
     ]
 
 
@@ -84,6 +86,11 @@ def _load():
                                         i64, p]),
         "thd_attn_fwd_noalloc": (ctypes.c_int, [p, p, p, p, p, p, p, i32, i32, i32, i32,
                                                 ctypes.c_float, p]),
+        "thd_build_pass_metadata": (ctypes.c_int, [pi32, i32, i32, i32, i32, i32, ctypes.c_uint64,
+                                                   i32, ctypes.POINTER(p)]),
+        "thd_attn_fwd_pass_workspace": (ctypes.c_int, [p, i32, i32, i32, pi64, pi64]),
+        "thd_attn_fwd_pass": (ctypes.c_int, [p, p, p, p, p, p, p, i32, i32, i32, i32, i32,
+                                             ctypes.c_float, p, i64, p]),
         "thd_attn_bwd_workspace": (ctypes.c_int, [p, i32, pi64]),
         "thd_attn_bwd": (ctypes.c_int, [p, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
                                         ctypes.c_float, p, i64, p]),
@@ -101,7 +108,10 @@ EXPORTS = ("thd_last_error", "thd_plan_partition", "thd_build_metadata", "thd_pa
            "thd_meta_copy", "thd_meta_release", "thd_cache_stats", "thd_cache_clear",
            "thd_preferred_tiles", "thd_preferred_fwd_tiles", "thd_fwd_concurrency",
            "thd_attn_fwd_workspace", "thd_attn_fwd", "thd_attn_fwd_noalloc",
+           "thd_build_pass_metadata", "thd_attn_fwd_pass_workspace", "thd_attn_fwd_pass",
            "thd_attn_bwd_workspace", "thd_attn_bwd")
+PASS_FIRST = 1
+PASS_LAST = 2
 
 
 def _check(code: int):
@@ -180,13 +190,16 @@ class Meta:
         n = {"q_global": inf["local_tokens"], "kv_row": inf["total_tokens"],
              "chunk_off": inf["n_docs"] * 2 * inf["cp"], "tiles": inf["n_tiles"] * 8,
              "order": inf["n_tiles"], "kvtiles": inf["n_kvtiles"] * 8,
-             "items": inf["n_items"] * 4, "splits": inf["n_splits"] * 4,
+             "items": inf["n_items"] * inf["item_ints"],
+             "splits": (inf["n_tiles"] if inf["is_pass"] else inf["n_splits"]) * 4,
              "doc_end": inf["n_docs"]}[name]
         out = np.empty(n, np.int32)
         _check(_lib.thd_meta_copy(self._h, FIELDS[name], _ptr32(out), n))
         if name in ("tiles", "kvtiles"):
             out = out.reshape(-1, 8)
-        if name in ("items", "splits"):
+        if name == "items":
+            out = out.reshape(-1, inf["item_ints"])
+        if name == "splits":
             out = out.reshape(-1, 4)
         return out
 
@@ -387,6 +400,71 @@ def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=No
                              None if ws is None else ws.data_ptr(), need,
                              _stream_handle(stream, dev)))
     return out, lse
+
+
+def build_pass_metadata(*, seqlens, cp: int, rank: int, block_t: int, block_n: int, shards,
+                        device: int = -1) -> Meta:
+    """Metadata of one forward pass over the keys of the listed source ranks'
+    shards (all-gather overlap; thd_build_pass_metadata)."""
+    lens = _lengths(seqlens)
+    mask = 0
+    for s_ in shards:
+        s_ = int(s_)
+        if not 0 <= s_ < 64:
+            raise ThdError(-1, "shard ranks must lie in [0, 64)")
+        mask |= 1 << s_
+    h = ctypes.c_void_p()
+    _check(_lib.thd_build_pass_metadata(_ptr32(lens), len(lens), cp, rank, block_t, block_n,
+                                        mask, device, ctypes.byref(h)))
+    return Meta(h)
+
+
+def pass_state(*, meta: Meta, hq: int, hkv: int, d_v: int, device):
+    """A state buffer (fp32) for the passes of one forward (thd_attn_fwd_pass_workspace)."""
+    torch = _torch()
+    state = ctypes.c_int64()
+    _check(_lib.thd_attn_fwd_pass_workspace(meta.handle, hq, hkv, d_v, None, ctypes.byref(state)))
+    return torch.empty(state.value // 4, dtype=torch.float32, device=device)
+
+
+def attn_fwd_pass(*, q, k, v, meta: Meta, state, first: bool, last: bool, out=None, lse=None,
+                  softmax_scale=None, stream=None):
+    """One pass of a shard-by-shard forward (thd_attn_fwd_pass): merges the
+    attention over the pass's shards into ``state``; with last=True writes and
+    returns (o, lse), else returns None. The rows of k and v outside the pass's
+    shards are not read."""
+    torch = _torch()
+    hq, hkv, d_qk, d_v = _qkv_shapes(q, k, v)
+    dev = q.device
+    inf = meta._cached_info()
+    if not inf["is_pass"]:
+        raise ThdError(-5, "metadata is not a pass plan")
+    t_loc, total = inf["local_tokens"], inf["total_tokens"]
+    _need("q", q, torch.bfloat16, (t_loc, hq, d_qk), dev)
+    _need("k", k, torch.bfloat16, (total, hkv, d_qk), dev)
+    _need("v", v, torch.bfloat16, (total, hkv, d_v), dev)
+    _need("state", state, torch.float32, (t_loc * hq * (d_v + 1),), dev)
+    if last:
+        if out is None:
+            out = torch.empty((t_loc, hq, d_v), dtype=torch.bfloat16, device=dev)
+        else:
+            _need("out", out, torch.bfloat16, (t_loc, hq, d_v), dev)
+        if lse is None:
+            lse = torch.empty((t_loc, hq), dtype=torch.float32, device=dev)
+        else:
+            _need("lse", lse, torch.float32, (t_loc, hq), dev)
+    parts = ctypes.c_int64()
+    _check(_lib.thd_attn_fwd_pass_workspace(meta.handle, hq, hkv, d_v, ctypes.byref(parts), None))
+    ws = _scratch(dev, parts.value, stream)
+    flags = (PASS_FIRST if first else 0) | (PASS_LAST if last else 0)
+    scale = 0.0 if softmax_scale is None else float(softmax_scale)
+    _check(_lib.thd_attn_fwd_pass(meta.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  None if out is None else out.data_ptr(),
+                                  None if lse is None else lse.data_ptr(), state.data_ptr(), flags,
+                                  hq, hkv, d_qk, d_v, scale,
+                                  None if ws is None else ws.data_ptr(), parts.value,
+                                  _stream_handle(stream, dev)))
+    return (out, lse) if last else None
 
 
 def attn_fwd_noalloc(*, q, k, v, out, lse, meta: Meta, out_f32=None, softmax_scale=None,

@@ -27,7 +27,13 @@ struct Plan {
   int32_t cp = 1, rank = 0, block_t = 1, block_n = 1, concurrency = 0, kv_split = 0;
   int64_t total = 0, local = 0, useful_pairs = 0, max_kv_tiles = 0, n_part_slots = 0;
   int64_t pad_tokens = 0;
+  // A pass plan (all-gather overlap) covers only the keys of the source ranks
+  // in shard_mask: its items are 8 ints with absolute key ranges, and splits
+  // holds one [tile, first part slot, parts, 0] record per tile.
+  bool pass = false;
+  uint64_t shard_mask = 0;
   std::vector<int32_t> q_global, kv_row, chunk_off, tiles, order, kvtiles, items, splits, doc_end;
+  int item_ints() const { return pass ? 8 : 4; }
 };
 
 // Checks lengths/cp/rank; throws Error. Returns T.
@@ -42,6 +48,13 @@ void plan_partition(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t 
 std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t cp,
                                  int32_t rank, int32_t block_t, int32_t block_n,
                                  int32_t concurrency, const int32_t* real_lengths);
+
+// The plan of one forward pass over the keys held by the source ranks in
+// shard_mask (bit s = rank s's shard): same tiles, items over maximal runs of
+// such chunks (see build_pass_plan).
+std::unique_ptr<Plan> build_pass_plan(const int32_t* seqlens, int32_t n_docs, int32_t cp,
+                                      int32_t rank, int32_t block_t, int32_t block_n,
+                                      uint64_t shard_mask);
 
 // Device copies of the arrays the kernels read.
 struct DeviceMeta {
@@ -98,6 +111,12 @@ struct FwdParams {
   int32_t n_items, n_splits, hq, hkv, group, block_t, block_n;
   int64_t total;
   float scale_log2;   // softmax_scale * log2(e)
+  // Pass plans only: items carry absolute key ranges; the running state
+  // (O [T_local, Hq, d_v] fp32 then its log2-sum-exp [T_local, Hq]) and the
+  // THD_PASS_FIRST / THD_PASS_LAST flags; n_splits counts every tile.
+  int32_t ranged, pass_flags;
+  float* state;
+  int64_t local;
 };
 
 #if defined(__HIPCC__)
@@ -123,6 +142,8 @@ int fwd_static_scratch(int device, void** ptr);
 
 // Kernel launchers (defined in the .hip files). Return a hipError_t value.
 int launch_fwd(const FwdParams& p, int d_qk, int d_v, void* stream);
+// One forward pass of a pass plan (its items, then the merge into the state).
+int launch_fwd_pass(const FwdParams& p, int d_qk, int d_v, void* stream);
 // Workgroups of the forward kernel for this KV tile size that fit one CU.
 int fwd_workgroups_per_cu(int block_n);
 

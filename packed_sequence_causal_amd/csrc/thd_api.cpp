@@ -115,9 +115,11 @@ Cache& cache() {
 
 std::string make_key(const int32_t* seqlens, const int32_t* real, int32_t n_docs, int32_t cp,
                      int32_t rank, int32_t block_t, int32_t block_n, int32_t concurrency,
-                     int32_t device) {
-  const int32_t head[9] = {THD_META_VERSION, cp,     rank,    block_t,          block_n,
-                           concurrency,      device, n_docs, real != nullptr ? 1 : 0};
+                     int32_t device, bool pass, uint64_t shard_mask) {
+  const int32_t head[12] = {THD_META_VERSION, cp,     rank,    block_t,
+                            block_n,          concurrency, device, n_docs,
+                            real != nullptr ? 1 : 0, pass ? 1 : 0, int32_t(shard_mask & 0xffffffffu),
+                            int32_t(shard_mask >> 32)};
   const size_t n = size_t(n_docs) * sizeof(int32_t);
   std::string key(sizeof(head) + (real != nullptr ? 2 : 1) * n, '\0');
   std::memcpy(&key[0], head, sizeof(head));
@@ -208,7 +210,8 @@ void pad_lengths(const int32_t* real, int32_t n_docs, int32_t cp, int32_t* padde
 // Shared by thd_build_metadata (real = NULL) and thd_build_metadata_padded.
 void build_metadata_impl(const int32_t* seqlens, const int32_t* real, int32_t n_docs, int32_t cp,
                          int32_t rank, int32_t block_t, int32_t block_n, int32_t concurrency,
-                         int32_t device, thd_meta** out) {
+                         int32_t device, thd_meta** out, bool pass = false,
+                         uint64_t shard_mask = 0) {
   if (out == nullptr) fail(THD_EINVAL, "out is NULL");
   *out = nullptr;
   validate_partition(seqlens, n_docs, cp, rank);
@@ -219,8 +222,8 @@ void build_metadata_impl(const int32_t* seqlens, const int32_t* real, int32_t n_
     check_hip(hipGetDeviceCount(&count), "hipGetDeviceCount");
     if (device >= count) fail(THD_EINVAL, "no such device " + std::to_string(device));
   }
-  const std::string key =
-      make_key(seqlens, real, n_docs, cp, rank, block_t, block_n, concurrency, device);
+  const std::string key = make_key(seqlens, real, n_docs, cp, rank, block_t, block_n,
+                                   concurrency, device, pass, shard_mask);
   Cache& c = cache();
   std::lock_guard<std::mutex> lock(c.mu);
   auto hit = c.map.find(key);
@@ -233,7 +236,8 @@ void build_metadata_impl(const int32_t* seqlens, const int32_t* real, int32_t n_
   } else {
     ++c.misses;
     auto e = std::make_shared<MetaEntry>();
-    e->plan = build_plan(seqlens, n_docs, cp, rank, block_t, block_n, concurrency, real);
+    e->plan = pass ? build_pass_plan(seqlens, n_docs, cp, rank, block_t, block_n, shard_mask)
+                   : build_plan(seqlens, n_docs, cp, rank, block_t, block_n, concurrency, real);
     if (device >= 0) {
       upload(*e, device);
       ++c.uploads;
@@ -322,7 +326,7 @@ int thd_meta_info(const thd_meta* meta, thd_meta_info_t* info) {
     info->n_kvtiles = int64_t(p.kvtiles.size() / 8);
     info->useful_pairs = p.useful_pairs;
     info->max_kv_tiles = p.max_kv_tiles;
-    info->n_items = int64_t(p.items.size() / 4);
+    info->n_items = int64_t(p.items.size() / p.item_ints());
     info->n_splits = int64_t(p.splits.size() / 4);
     info->n_part_slots = p.n_part_slots;
     info->pad_tokens = p.pad_tokens;
@@ -336,6 +340,9 @@ int thd_meta_info(const thd_meta* meta, thd_meta_info_t* info) {
     info->version = THD_META_VERSION;
     info->device = e.dev.base != nullptr ? e.dev.device : -1;
     info->cache_hit = meta->cache_hit ? 1 : 0;
+    info->is_pass = p.pass ? 1 : 0;
+    info->item_ints = p.item_ints();
+    info->shard_mask = p.shard_mask;
   });
 }
 
@@ -493,6 +500,7 @@ void attn_fwd_impl(const thd_meta* meta, const void* q, const void* k, const voi
   softmax_scale = resolve_scale(softmax_scale, d_qk);
   const int32_t group = hq / hkv;
   check_fwd_tiles(p, group, d_qk);
+  if (p.pass) fail(THD_EMISMATCH, "metadata is a pass plan: call thd_attn_fwd_pass");
   check_ptr(q, "q", 16);
   check_ptr(k, "k", 16);
   check_ptr(v, "v", 16);
@@ -572,6 +580,99 @@ int thd_attn_fwd_noalloc(const thd_meta* meta, const void* q, const void* k, con
   });
 }
 
+int thd_build_pass_metadata(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank,
+                            int32_t block_t, int32_t block_n, uint64_t shard_mask,
+                            int32_t device, thd_meta** out) {
+  return guarded([&] {
+    build_metadata_impl(seqlens, nullptr, n_docs, cp, rank, block_t, block_n, 0, device, out,
+                        true, shard_mask);
+  });
+}
+
+int thd_attn_fwd_pass_workspace(const thd_meta* meta, int32_t hq, int32_t hkv, int32_t d_v,
+                                int64_t* parts_bytes, int64_t* state_bytes) {
+  return guarded([&] {
+    const Plan& p = *entry_of(meta).plan;
+    check_heads(hq, hkv);
+    if (d_v < 1) fail(THD_EINVAL, "d_v must be >= 1");
+    if (!p.pass) fail(THD_EMISMATCH, "metadata is not a pass plan");
+    if (parts_bytes != nullptr)
+      *parts_bytes = p.n_part_slots * hkv * fwd_partial_floats(p.block_t, hq / hkv, d_v) *
+                     int64_t(sizeof(float));
+    if (state_bytes != nullptr) *state_bytes = p.local * hq * (int64_t(d_v) + 1) * int64_t(sizeof(float));
+  });
+}
+
+int thd_attn_fwd_pass(const thd_meta* meta, const void* q, const void* k, const void* v, void* o,
+                      float* lse, float* state, int32_t flags, int32_t hq, int32_t hkv,
+                      int32_t d_qk, int32_t d_v, float softmax_scale, void* workspace,
+                      int64_t workspace_bytes, void* hip_stream) {
+  return guarded([&] {
+    const MetaEntry& e = entry_of(meta);
+    const Plan& p = *e.plan;
+    check_heads(hq, hkv);
+    if (!fwd_supported(d_qk, d_v))
+      fail(THD_EUNSUPPORTED, "no forward kernel for d_qk=" + std::to_string(d_qk) +
+                                 ", d_v=" + std::to_string(d_v));
+    softmax_scale = resolve_scale(softmax_scale, d_qk);
+    if (!p.pass) fail(THD_EMISMATCH, "metadata is not a pass plan (thd_build_pass_metadata)");
+    if (p.block_n != kBlockN)
+      fail(THD_EMISMATCH, "pass plans take block_n = " + std::to_string(kBlockN));
+    if ((flags & ~(THD_PASS_FIRST | THD_PASS_LAST)) != 0) fail(THD_EINVAL, "unknown pass flags");
+    const int32_t group = hq / hkv;
+    check_fwd_tiles(p, group, d_qk);
+    check_ptr(q, "q", 16);
+    check_ptr(k, "k", 16);
+    check_ptr(v, "v", 16);
+    check_ptr(state, "state", 16);
+    if (flags & THD_PASS_LAST) {
+      check_ptr(o, "o", 16);
+      check_ptr(lse, "lse", 16);
+    }
+    const int64_t need = p.n_part_slots * hkv * fwd_partial_floats(p.block_t, group, d_v) *
+                         int64_t(sizeof(float));
+    if (need > 0) {
+      check_ptr(workspace, "workspace", 16);
+      if (workspace_bytes < need)
+        fail(THD_EINVAL, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
+                             std::to_string(need));
+    }
+    const DeviceMeta& d = device_meta(e);
+    const int64_t n_items = int64_t(p.items.size() / 8);
+    const int64_t n_tiles = int64_t(p.tiles.size() / 8);
+    if (n_items * hkv >= (int64_t(1) << 31) || n_tiles * hkv >= (int64_t(1) << 31))
+      fail(THD_ERANGE, "grid too large");
+    check_kv_bytes(p.total, hkv, d_qk, d_v);
+    FwdParams fp{};
+    fp.q = q;
+    fp.k = k;
+    fp.v = v;
+    fp.o = o;
+    fp.lse = lse;
+    fp.o_f32 = nullptr;
+    fp.partial = static_cast<float*>(workspace);
+    fp.tiles = d.tiles;
+    fp.items = d.items;
+    fp.splits = d.splits;
+    fp.kv_row = d.kv_row;
+    fp.doc_end = d.doc_end;
+    fp.n_items = int32_t(n_items);
+    fp.n_splits = int32_t(n_tiles);
+    fp.hq = hq;
+    fp.hkv = hkv;
+    fp.group = group;
+    fp.block_t = p.block_t;
+    fp.block_n = p.block_n;
+    fp.total = p.total;
+    fp.scale_log2 = softmax_scale * 1.4426950408889634f;
+    fp.ranged = 1;
+    fp.pass_flags = flags;
+    fp.state = state;
+    fp.local = p.local;
+    check_hip(hipError_t(launch_fwd_pass(fp, d_qk, d_v, hip_stream)), "forward pass launch");
+  });
+}
+
 int thd_attn_bwd_workspace(const thd_meta* meta, int32_t hq, int64_t* bytes) {
   return guarded([&] {
     const Plan& p = *entry_of(meta).plan;
@@ -596,6 +697,7 @@ int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void*
     softmax_scale = resolve_scale(softmax_scale, d_qk);
     const int32_t group = hq / hkv;
     check_bwd_tiles(p, group);
+    if (p.pass) fail(THD_EMISMATCH, "metadata is a pass plan, not the full key range");
     check_ptr(q, "q", 16);
     check_ptr(k, "k", 16);
     check_ptr(v, "v", 16);

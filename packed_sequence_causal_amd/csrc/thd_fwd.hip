@@ -140,7 +140,9 @@ struct FwdShape {
 template <int BN>
 constexpr int kFwdOccupancy = BN == kBlockNShort ? 3 : 2;
 
-template <int DQK, int DV, bool EXACT, int BN_>
+// RANGED: items of a pass plan (all-gather overlap), 8 ints with an absolute
+// key range [first key, end key) per item, always written as a part.
+template <int DQK, int DV, bool EXACT, int BN_, bool RANGED = false>
 __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kernel(FwdParams p) {
   using S = FwdShape<DQK, DV, BN_>;
   constexpr int BN = S::BN;
@@ -162,21 +164,24 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
   // Work item: KV tiles [kv_begin, kv_end) of one query tile (a whole tile
   // unless its key range is split), for kv head blockIdx.x % Hkv.
   const int kvh = blockIdx.x % p.hkv;
-  const int32_t* item = p.items + size_t(blockIdx.x / p.hkv) * 4;
+  const int32_t* item = p.items + size_t(blockIdx.x / p.hkv) * (RANGED ? 8 : 4);
   const int tile = item[0];
-  const int kv_begin = item[1];
-  const int kv_end = item[2];
+  const int kv_begin = RANGED ? 0 : item[1];
+  const int kv_end = RANGED ? item[4] : item[2];
   const int part = item[3];
   const int32_t* td = p.tiles + size_t(tile) * 8;
   const int q_local0 = td[0];
   const int q_glob0 = td[1];
   const int n_rows = td[2];
-  const int kv_start = td[5];
-  const int n_full = td[7];
+  // KV tiles start at the document's first key (a pass plan's item: at its
+  // run's first key); keys from key_hi on are seen by no row of the item.
+  const int kv_start = RANGED ? item[1] : td[5];
+  const int n_full = RANGED ? item[5] : td[7];
+  const int key_hi = RANGED ? item[2] : q_glob0 + n_rows;
   // Rows at or past the document's last real token are padding: written as
   // O = 0, LSE = +inf (tokens are in position order within a tile).
   const int n_real = min(max(p.doc_end[td[3]] - q_glob0, 0), n_rows);
-  const int key_last = q_glob0 + n_rows - 1;   // keys past this are seen by no row
+  const int key_last = key_hi - 1;
 
   // Row block rb of this wave holds rows 32 * (RB * wave + rb) + lane % 32.
   const int G = p.group;
@@ -189,7 +194,8 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
     tok[rb] = row / G;
     head[rb] = kvh * G + (row - tok[rb] * G);
     valid[rb] = tok[rb] < n_rows;
-    qpos[rb] = valid[rb] ? q_glob0 + tok[rb] : INT_MAX;
+    // The causal compare also ends a pass item's range at key_hi.
+    qpos[rb] = valid[rb] ? (RANGED ? min(q_glob0 + tok[rb], key_last) : q_glob0 + tok[rb]) : INT_MAX;
     rb_active[rb] = row0 / G < n_rows;          // wave-uniform
   }
   const bool wave_active = rb_active[0];
@@ -613,6 +619,101 @@ __global__ __launch_bounds__(256) void thd_fwd_combine_kernel(FwdParams p) {
   if (col == 0) p.lse[orow] = pad ? INFINITY : (mx + __builtin_amdgcn_logf(wsum)) * kLn2;
 }
 
+// Merges a pass's parts into the running state: per row, the state's
+// (O, lse2) and each part's, weighted by 2^(lse2 - max) (THD_PASS_FIRST: the
+// state counts as empty). THD_PASS_LAST writes O (bf16; pad rows 0) and LSE
+// (natural log; pad rows +inf); otherwise the merged state. One thread per
+// (tile, kv head, row, 4 columns). The threads of one row lie in one wave (a
+// row's DV / 4 threads are consecutive and divide 64): the state's lse2 of the
+// row is loaded by all of them in one instruction before the row's first
+// thread stores the new one, which depends on that load.
+template <int DV>
+__global__ __launch_bounds__(256) void thd_fwd_pass_combine_kernel(FwdParams p) {
+  constexpr int CPR = DV / 4;
+  static_assert(64 % CPR == 0, "a row's threads must lie in one wave");
+  const int G = p.group;
+  const int rows = p.block_t * G;
+  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t per_tile = int64_t(p.hkv) * rows * CPR;
+  if (idx >= per_tile * p.n_splits) return;
+  const int t = int(idx / per_tile);
+  int rem = int(idx - t * per_tile);
+  const int kvh = rem / (rows * CPR);
+  rem -= kvh * rows * CPR;
+  const int row = rem / CPR;
+  const int col = (rem - row * CPR) * 4;
+  const int32_t* sp = p.splits + size_t(t) * 4;
+  const int tile = sp[0], first = sp[1], n_parts = sp[2];
+  const bool first_pass = (p.pass_flags & THD_PASS_FIRST) != 0;
+  const bool last = (p.pass_flags & THD_PASS_LAST) != 0;
+  if (n_parts == 0 && !last && !first_pass) return;   // the state stays as it is
+  const int32_t* td = p.tiles + size_t(tile) * 8;
+  const int tok = row / G;
+  if (tok >= td[2]) return;
+  const int head = kvh * G + (row - tok * G);
+  const size_t orow = size_t(td[0] + tok) * p.hq + head;
+  float* st_o = p.state + orow * DV + col;
+  float* st_l = p.state + size_t(p.local) * p.hq * DV + orow;
+  const float ls = first_pass ? -INFINITY : *st_l;
+  const size_t slot_floats = size_t(fwd_partial_floats(p.block_t, G, DV));
+  const float* base0 = p.partial + (size_t(first) * p.hkv + kvh) * slot_floats;
+  const size_t part_stride = size_t(p.hkv) * slot_floats;
+  float mx = ls;
+  for (int q = 0; q < n_parts; ++q) mx = fmaxf(mx, base0[q * part_stride + size_t(rows) * DV + row]);
+  f32x4 o4 = {};
+  float lnew = -INFINITY;
+  if (mx > -INFINITY) {
+    float wsum = 0.0f;
+    f32x4 acc = {};
+    if (ls > -INFINITY) {
+      const float w = __builtin_amdgcn_exp2f(ls - mx);
+      wsum += w;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(st_o);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = w * v[e];
+    }
+    for (int q = 0; q < n_parts; ++q) {
+      const float* base = base0 + q * part_stride;
+      const float w = __builtin_amdgcn_exp2f(base[size_t(rows) * DV + row] - mx);
+      wsum += w;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(base + size_t(row) * DV + col);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, v[e], acc[e]);
+    }
+    const float inv = 1.0f / wsum;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o4[e] = acc[e] * inv;
+    lnew = mx + __builtin_amdgcn_logf(wsum);
+  }
+  if (last) {
+    const bool pad = td[1] + tok >= p.doc_end[td[3]];
+    bf16x4 out;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) out[e] = static_cast<__bf16>(pad ? 0.0f : o4[e]);
+    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.o) + orow * DV + col) = out;
+    if (col == 0) p.lse[orow] = pad ? INFINITY : lnew * kLn2;
+  } else {
+    *reinterpret_cast<f32x4*>(st_o) = o4;
+    if (col == 0) *st_l = lnew;
+  }
+}
+
+template <int DQK, int DV>
+int launch_pass(const FwdParams& p, void* stream) {
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (p.n_items > 0) {
+    hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV, false, kBlockN, true>),
+                       dim3(unsigned(int64_t(p.n_items) * p.hkv)), dim3(kFwdThreads), 0, st, p);
+    const hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return int(err);
+  }
+  const int64_t threads = int64_t(p.n_splits) * p.hkv * p.block_t * p.group * (DV / 4);
+  if (threads == 0) return int(hipSuccess);
+  hipLaunchKernelGGL((thd_fwd_pass_combine_kernel<DV>), dim3(unsigned((threads + 255) / 256)),
+                     dim3(256), 0, st, p);
+  return int(hipGetLastError());
+}
+
 template <int DQK, int DV, int BN>
 int launch(const FwdParams& p, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -671,6 +772,13 @@ bool fwd_block_n_supported(int d_qk, int block_n) {
 
 int fwd_workgroups_per_cu(int block_n) {
   return block_n == kBlockNShort ? kFwdOccupancy<kBlockNShort> : kFwdOccupancy<kBlockN>;
+}
+
+int launch_fwd_pass(const FwdParams& p, int d_qk, int d_v, void* stream) {
+  if (d_qk == 64 && d_v == 64) return launch_pass<64, 64>(p, stream);
+  if (d_qk == 128 && d_v == 128) return launch_pass<128, 128>(p, stream);
+  if (d_qk == 192 && d_v == 128) return launch_pass<192, 128>(p, stream);
+  return int(hipErrorInvalidValue);
 }
 
 int launch_fwd(const FwdParams& p, int d_qk, int d_v, void* stream) {

@@ -213,4 +213,61 @@ std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t
   return plan;
 }
 
+std::unique_ptr<Plan> build_pass_plan(const int32_t* seqlens, int32_t n_docs, int32_t cp,
+                                      int32_t rank, int32_t block_t, int32_t block_n,
+                                      uint64_t shard_mask) {
+  validate_partition(seqlens, n_docs, cp, rank);
+  if (cp > 64) fail(THD_ERANGE, "pass plans take cp <= 64 (one mask bit per source rank)");
+  if (shard_mask == 0 || (cp < 64 && (shard_mask >> cp) != 0))
+    fail(THD_EINVAL, "shard_mask must name at least one source rank, and only ranks < cp");
+  auto plan = build_plan(seqlens, n_docs, cp, rank, block_t, block_n, 0, nullptr);
+  Plan& p = *plan;
+  p.pass = true;
+  p.shard_mask = shard_mask;
+  p.items.clear();
+  p.splits.clear();
+  p.n_part_slots = 0;
+  p.kv_split = 0;
+  // Chunk k of a document is held by source rank min(k, 2cp-1-k). A tile of
+  // chunk k's rows sees chunks 0..k; each maximal run [a, b] of those held by
+  // a rank in the mask is one work item, from the run's first key to the end
+  // of chunk b (or to the tile's last row when b is the rows' own chunk).
+  auto held = [&](int64_t chunk) {
+    const int64_t owner = std::min<int64_t>(chunk, 2 * int64_t(cp) - 1 - chunk);
+    return ((shard_mask >> owner) & 1u) != 0;
+  };
+  const int64_t n_tiles = int64_t(p.tiles.size() / 8);
+  std::vector<int32_t> natural;
+  for (int64_t t = 0; t < n_tiles; ++t) {
+    const int32_t* rec = &p.tiles[size_t(t) * 8];
+    const int64_t q_glob = rec[1], n_rows = rec[2], doc = rec[3], slot = rec[4], cu = rec[5];
+    const int64_t c = seqlens[doc] / (2 * int64_t(cp));
+    const int64_t k = slot == 0 ? rank : 2 * int64_t(cp) - 1 - rank;
+    const int64_t first = p.n_part_slots;
+    for (int64_t chunk = 0; chunk <= k; ++chunk) {
+      if (!held(chunk)) continue;
+      const int64_t a = chunk;
+      while (chunk + 1 <= k && held(chunk + 1)) ++chunk;
+      const int64_t lo = cu + a * c;
+      const int64_t hi = chunk < k ? cu + (chunk + 1) * c : q_glob + n_rows;
+      const int64_t n_kv = (hi - lo + block_n - 1) / block_n;
+      const int64_t n_full = std::min((q_glob - lo + 1) / block_n, (hi - lo) / block_n);
+      const int32_t item[8] = {int32_t(t),    int32_t(lo),   int32_t(hi), int32_t(p.n_part_slots++),
+                               int32_t(n_kv), int32_t(n_full), 0,         0};
+      natural.insert(natural.end(), item, item + 8);
+    }
+    const int32_t srec[4] = {int32_t(t), int32_t(first), int32_t(p.n_part_slots - first), 0};
+    p.splits.insert(p.splits.end(), srec, srec + 4);
+  }
+  const int64_t n_items = int64_t(natural.size() / 8);
+  std::vector<int32_t> idx(n_items);
+  std::iota(idx.begin(), idx.end(), 0);
+  std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) {
+    return natural[size_t(a) * 8 + 4] > natural[size_t(b) * 8 + 4];
+  });
+  p.items.reserve(natural.size());
+  for (int32_t i : idx) p.items.insert(p.items.end(), &natural[size_t(i) * 8], &natural[size_t(i) * 8] + 8);
+  return plan;
+}
+
 }  // namespace thd

@@ -7,6 +7,7 @@
 
 namespace thd {
 int launch_fwd(const FwdParams&, int, int, void*) { return int(hipErrorInvalidValue); }
+int launch_fwd_pass(const FwdParams&, int, int, void*) { return int(hipErrorInvalidValue); }
 int launch_bwd(const BwdParams&, int, int, void*) { return int(hipErrorInvalidValue); }
 bool fwd_supported(int, int) { return false; }
 bool bwd_supported(int, int) { return false; }

@@ -398,3 +398,55 @@ def test_pad_lengths_errors(kwargs, status):
     assert e.value.status == status
     with pytest.raises(thd.ThdError):
         thd.build_metadata(block_t=8, block_n=16, rank=0, padded=True, **kwargs)
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_pass_plans_match_oracle_bit_for_bit(seed):
+    rng = np.random.default_rng(500 + seed)
+    cp = int(rng.choice([1, 2, 3, 4, 8]))
+    rank = int(rng.integers(0, cp))
+    lengths = [2 * cp * int(x) for x in rng.integers(1, 40, size=int(rng.integers(1, 9)))]
+    bt = int(rng.choice([4, 16, 32, 128]))
+    bn = 64
+    shards = sorted({int(x) for x in rng.integers(0, cp, size=int(rng.integers(1, cp + 1)))})
+    m = thd.build_pass_metadata(seqlens=lengths, cp=cp, rank=rank, block_t=bt, block_n=bn,
+                                shards=shards)
+    info = m.info()
+    assert info["is_pass"] == 1 and info["item_ints"] == 8
+    assert info["shard_mask"] == sum(1 << s for s in shards)
+    want_items, want_tiles = ometa.pass_plan(lengths, cp, rank, bt, bn, shards)
+    assert np.array_equal(m.field("items"), want_items)
+    assert np.array_equal(m.field("splits"), want_tiles)
+    assert np.array_equal(m.field("tiles"), ometa.tiles(lengths, cp, rank, bt, bn))
+    assert info["n_part_slots"] == want_items.shape[0]
+    # the mask is part of the cache key
+    other = thd.build_pass_metadata(seqlens=lengths, cp=cp, rank=rank, block_t=bt, block_n=bn,
+                                    shards=[s for s in range(cp) if s not in shards] or shards)
+    if set(shards) != set(range(cp)):
+        assert other.info()["shard_mask"] != info["shard_mask"]
+
+
+def test_pass_metadata_errors():
+    lib = thd._lib
+    for shards in ([], [2]):   # no shard; a shard beyond cp
+        with pytest.raises(thd.ThdError) as err:
+            thd.build_pass_metadata(seqlens=[8, 16], cp=2, rank=0, block_t=4, block_n=64,
+                                    shards=shards)
+        assert err.value.status == "THD_EINVAL"
+    with pytest.raises(thd.ThdError) as err:
+        thd.build_pass_metadata(seqlens=[6], cp=2, rank=0, block_t=4, block_n=64, shards=[0])
+    assert err.value.status == "THD_ENOTDIV"
+    # a pass plan is refused by the one-pass entry points, and the reverse
+    buf = ctypes.create_string_buffer(1 << 16)
+    ptr = (ctypes.addressof(buf) + 15) // 16 * 16
+    mp = thd.build_pass_metadata(seqlens=[256], cp=1, rank=0, block_t=32, block_n=64, shards=[0])
+    assert lib.thd_attn_fwd(mp.handle, ptr, ptr, ptr, ptr, ptr, None, 32, 8, 128, 128, 0.0, None,
+                            0, None) == -5
+    assert b"pass" in lib.thd_last_error()
+    m = thd.build_metadata(seqlens=[256], cp=1, rank=0, block_t=32, block_n=64)
+    assert lib.thd_attn_fwd_pass(m.handle, ptr, ptr, ptr, ptr, ptr, ptr, 3, 32, 8, 128, 128, 0.0,
+                                 None, 0, None) == -5
+    assert lib.thd_attn_fwd_pass(mp.handle, ptr, ptr, ptr, ptr, ptr, ptr, 4, 32, 8, 128, 128, 0.0,
+                                 None, 0, None) == -1
+    n = ctypes.c_int64()
+    assert lib.thd_attn_fwd_pass_workspace(m.handle, 32, 8, 128, ctypes.byref(n), None) == -5
