@@ -461,8 +461,9 @@ int thd_fwd_concurrency(int32_t device, int32_t hkv, int32_t block_n, int32_t* c
     check_hip(hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device),
               "hipDeviceGetAttribute");
     // Seven eighths of the slots: parts then come out a little longer and
-    // fewer, which pays for their startup and the combine pass (MLA workload,
-    // 9 documents of 1024-8192 tokens, cp = 8: 156 against 160 us; the split
+    // fewer, which saves part startups and combine traffic (MLA workload, 9
+    // documents of 1024-8192 tokens, cp = 8: 8 split tiles instead of 13,
+    // kernel plus combine about 1% faster, within run-to-run spread; the split
     // rule does not split at all below about five eighths there).
     *concurrency = std::max(1, cus * fwd_workgroups_per_cu(block_n) * 7 / (8 * hkv));
   });
