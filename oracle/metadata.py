@@ -5,7 +5,7 @@ Test infrastructure only (see the package docstring).
 The subject page ("kvallgather cp thd load balance", section "What this PR does
 / why we need it?") says metadata is cached to avoid repeated computation but
 gives no format. The format below is this project's interface contract between
-the host planner and the GPU kernels (version 3). It is unique given
+the host planner and the GPU kernels (version 4). It is unique given
 (lengths, cp, rank, BT, BN, concurrency), so the host library must reproduce it bit for bit.
 
 Definitions (all integer, floor division of non-negative values):
@@ -56,6 +56,35 @@ The key tiles cover every key once. Keys of document i at offset >=
 (2cp-r)*c_i are seen by no local query (the rank's later chunk is 2cp-1-r), so
 tiles made only of such keys get the empty range q_begin = q_end.
 
+Packed forward plans (version 4; short-segment packing, a reading of the
+column-wise [start, end) key bounds per row of the FlashMask kernels named on
+"[Optim] FlashMask-4 Overlap support part 1 (NVSHMEM backend) - #166"). A
+(document, slot) whose chunk length is not a multiple of BT leaves one
+partial tile, its last. With key_cap = BN * (largest n_kv over all tiles),
+the partial tiles are taken in tile order and grouped greedily. A tile of
+document i adds keys add = kv_len - kv_len(prev) when the group's previous
+member is also of document i (its keys are then a prefix of this tile's) and
+add = kv_len otherwise; it joins the open group while the group's tokens plus
+n_rows stay <= BT and the group's keys plus add stay <= key_cap, else the
+group closes and a new one opens with it. A group of one tile stays as it is;
+each larger group becomes one packed tile. The plan's tiles are the tiles in
+no larger group (tile order), then the packed tiles (group order); order and
+the work items are then formed over this list as above (a packed tile has
+n_full = 0, so it is never split).
+A packed tile lays its documents' keys out one document after the other: a
+document's block starts at slot base_i and holds keys cu_i .. cu_i + K_i - 1,
+K_i the kv_len of its last member. The member's row o (global position
+g = q_glob + o) sees slots base_i .. base_i + (g - cu_i), exactly its causal
+keys. Both window ends grow along the packed rows. Records:
+    packed tile     = [-1, first pack row, tokens, -1, -1, first pack key,
+                       n_kv = ceil(slots / BN), 0]
+    pack_rows[.][4] = [local row, first visible slot, last visible slot,
+                       1 if g < doc_end_i else 0], one per packed row, members
+                       in group order
+    pack_keys[.]    = gathered row (kv_row) of each slot's key, the tile's
+                       slots padded to whole KV tiles with its last slot's
+                       row (seen by no row)
+
 Pass plans (all-gather overlap; a reading of "[Optim] FlashMask-4 Overlap
 support part 1 (NVSHMEM backend) - #166", feature list, "AG fwd overlap"): a
 forward pass over the keys of a set S of source ranks' shards. For each tile
@@ -81,7 +110,7 @@ import numpy as np
 
 from . import partition
 
-VERSION = 3
+VERSION = 4
 TILE_FIELDS = ("q_local_start", "q_global_start", "n_rows", "doc", "slot",
                "kv_start", "n_kv_tiles", "n_full_kv_tiles")
 KVTILE_FIELDS = ("doc", "kv_global_start", "n_keys", "q_tile_begin", "q_tile_end",
@@ -241,3 +270,74 @@ def pass_plan(seqlens, cp: int, rank: int, block_t: int, block_n: int, shards):
     ranked = sorted(range(len(natural)), key=lambda j: (-natural[j][4], j))
     items = np.asarray([natural[j] for j in ranked], dtype=np.int32).reshape(-1, 8)
     return items, np.asarray(table, dtype=np.int32).reshape(-1, 4)
+
+
+def packed_plan(seqlens, cp: int, rank: int, block_t: int, block_n: int, real_lengths=None):
+    """(tiles, pack_rows, pack_keys) of a packed forward plan (module docstring)."""
+    lengths = partition.validate(seqlens, cp, rank)
+    tt = tiles(lengths, cp, rank, block_t, block_n)
+    cu = partition.cu_seqlens(lengths)
+    rowmap = partition.kv_row(lengths, cp)
+    ends = doc_end(lengths, cp, real_lengths)
+    key_cap = block_n * max(int(x) for x in tt[:, 6])
+
+    def kv_len(t):
+        return int(tt[t, 1]) + int(tt[t, 2]) - int(tt[t, 5])
+
+    groups, group, g_tok, g_keys = [], [], 0, 0
+    for t in range(tt.shape[0]):
+        if int(tt[t, 2]) == block_t:
+            continue
+        same_doc = bool(group) and int(tt[group[-1], 3]) == int(tt[t, 3])
+        add = kv_len(t) - (kv_len(group[-1]) if same_doc else 0)
+        if group and g_tok + int(tt[t, 2]) <= block_t and g_keys + add <= key_cap:
+            group.append(t)
+            g_tok += int(tt[t, 2])
+            g_keys += add
+            continue
+        if group:
+            groups.append(group)
+        group, g_tok, g_keys = [t], int(tt[t, 2]), kv_len(t)
+    if group:
+        groups.append(group)
+
+    packed = {t for g in groups if len(g) > 1 for t in g}
+    out = [[int(x) for x in tt[t]] for t in range(tt.shape[0]) if t not in packed]
+    rows, keys = [], []
+    for g in groups:
+        if len(g) == 1:
+            continue
+        row0, key0 = len(rows), len(keys)
+        docs = []                       # (doc, base slot, K) in order
+        for t in g:
+            i = int(tt[t, 3])
+            if docs and docs[-1][0] == i:
+                docs[-1][2] = max(docs[-1][2], kv_len(t))
+            else:
+                docs.append([i, sum(d[2] for d in docs), kv_len(t)])
+        base = {d[0]: d[1] for d in docs}
+        for i, _, k_i in docs:
+            keys.extend(int(rowmap[cu[i] + x]) for x in range(k_i))
+        for t in g:
+            q_local, q_glob, n_rows, i = (int(x) for x in tt[t, :4])
+            for o in range(n_rows):
+                g_pos = q_glob + o
+                rows.append([q_local + o, base[i], base[i] + g_pos - cu[i],
+                             1 if g_pos < int(ends[i]) else 0])
+        slots = len(keys) - key0
+        n_kv = _ceil_div(slots, block_n)
+        keys.extend([keys[-1]] * (n_kv * block_n - slots))
+        out.append([-1, row0, len(rows) - row0, -1, -1, key0, n_kv, 0])
+    return (np.asarray(out, dtype=np.int32).reshape(-1, 8),
+            np.asarray(rows, dtype=np.int32).reshape(-1, 4),
+            np.asarray(keys, dtype=np.int32))
+
+
+def packed_forward_plan(seqlens, cp: int, rank: int, block_t: int, block_n: int,
+                        concurrency: int, real_lengths=None) -> dict:
+    """Every table of a packed forward plan: tiles, order, items, splits,
+    pack_rows, pack_keys (order and items over the packed tile list)."""
+    tt, rows, keys = packed_plan(seqlens, cp, rank, block_t, block_n, real_lengths)
+    items, splits = items_and_splits(tt, concurrency)
+    return {"tiles": tt, "order": order(tt), "items": items, "splits": splits,
+            "pack_rows": rows, "pack_keys": keys}
