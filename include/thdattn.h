@@ -62,7 +62,7 @@ typedef enum {
 } thd_status;
 
 /* Version of the tile-table contract (the per-tile bounds and work items below). */
-#define THD_META_VERSION 3
+#define THD_META_VERSION 4
 
 /* Fields of a metadata object, for thd_meta_copy. All int32.
  *   Q_GLOBAL  [T_local]       global packed position of each local query row
@@ -87,6 +87,13 @@ typedef enum {
  *   DOC_END   [n_docs]        global position one past each document's last
  *                             real token (cu_i + L_i without padding; see
  *                             thd_build_metadata_padded)
+ *   PACK_ROWS [n_pack_rows*4] packed plans (thd_build_packed_metadata): per row
+ *                             of the packed tiles, in tile order: local row,
+ *                             first and last key slot it sees, 1 if real
+ *                             (0 for a pad row)
+ *   PACK_KEYS [n_pack_keys]   packed plans: gathered row of each key slot;
+ *                             each packed tile's slots start at its
+ *                             kv_start and fill n_kv_tiles whole KV tiles
  * With concurrency C > 0 (work items of one kv head the device runs at once)
  * and fewer than 2C tiles, the key range of tiles longer than
  * kv_split = max(ceil(sum of n_kv_tiles / C), 8) KV tiles is cut into
@@ -102,7 +109,9 @@ enum {
   THD_FIELD_KVTILES = 5,
   THD_FIELD_ITEMS = 6,
   THD_FIELD_SPLITS = 7,
-  THD_FIELD_DOC_END = 8
+  THD_FIELD_DOC_END = 8,
+  THD_FIELD_PACK_ROWS = 9,
+  THD_FIELD_PACK_KEYS = 10
 };
 
 typedef struct thd_meta thd_meta;   /* opaque, library-owned, reference-counted */
@@ -125,6 +134,11 @@ typedef struct {
   int32_t is_pass;          /* 1 for a pass plan (thd_build_pass_metadata) */
   int32_t item_ints;        /* ints per ITEMS record: 4, or 8 for a pass plan */
   uint64_t shard_mask;      /* pass plans: bit s set = keys of rank s's shard */
+  int64_t n_packed_tiles;   /* packed plans: tiles made of several partial tiles */
+  int64_t n_pack_rows;      /* packed plans: rows of the packed tiles (PACK_ROWS) */
+  int64_t n_pack_keys;      /* packed plans: key slots (PACK_KEYS) */
+  int32_t is_packed;        /* 1 for a packed plan (thd_build_packed_metadata) */
+  int32_t reserved;
 } thd_meta_info_t;
 
 /* Message for the calling thread's last failed call ("" if none). An
@@ -183,6 +197,32 @@ int thd_pad_lengths(const int32_t* real_lengths, int32_t n_docs, int32_t cp, int
 int thd_build_metadata_padded(const int32_t* real_lengths, int32_t n_docs, int32_t cp,
                               int32_t rank, int32_t block_t, int32_t block_n,
                               int32_t concurrency, int32_t device, thd_meta** out);
+
+/* Short-segment packing: a forward plan whose last, partial query tiles of
+ * consecutive chunks are grouped into packed tiles. Reading of the per-row
+ * [start, end) key bounds of the FlashMask kernels on "[Optim] FlashMask-4
+ * Overlap support part 1 (NVSHMEM backend) - #166", applied to the documents
+ * of "feat: kvallgather cp thd load balance #3820". Plain tiles are those of
+ * thd_build_metadata; the partial tiles (fewer than block_t rows) are taken
+ * in tile order and a tile joins the open group while the group holds at most
+ * block_t rows and at most block_n * K key slots, K = max_kv_tiles or, when
+ * the plain tiles would be split (see THD_FIELD_ITEMS), the smaller of it and
+ * their kv_split: packed tiles are never split. (A tile of the same document
+ * as the group's previous member adds only the keys past that member's.) Each group of two or more becomes one packed tile, listed after
+ * the plain ones: TILES record [-1, first PACK_ROWS row, rows, -1, -1, first
+ * PACK_KEYS slot, n_kv_tiles, 0]. Its documents' keys take consecutive slots,
+ * one document after the other, and each row sees exactly its causal keys as
+ * one window of slots. ORDER and ITEMS are formed over this tile list as in
+ * thd_build_metadata (packed tiles are never split). The result is the same
+ * attention as the plain plan's, with fewer workgroups when many documents
+ * end in short tiles. Forward only: thd_attn_bwd refuses it (no KVTILES).
+ *   lengths[n_docs]: as seqlens of thd_build_metadata (padded = 0), or as
+ *   real_lengths of thd_build_metadata_padded (padded = 1). Other arguments,
+ *   the cache and the errors as thd_build_metadata, plus THD_EINVAL for padded
+ *   not 0 or 1. */
+int thd_build_packed_metadata(const int32_t* lengths, int32_t n_docs, int32_t cp, int32_t rank,
+                              int32_t block_t, int32_t block_n, int32_t concurrency,
+                              int32_t padded, int32_t device, thd_meta** out);
 
 /* Sizes and counters of a metadata object (see thd_meta_info_t); the
  * metadata of "feat: kvallgather cp thd load balance #3820", "What this PR
@@ -253,8 +293,9 @@ int thd_attn_fwd_workspace(const thd_meta* meta, int32_t hq, int32_t hkv, int32_
  * why we need it?" (THD attention with direct rank-major K/V indexing in a
  * single fused call; MHA, GQA, expanded MLA) and "Does this PR introduce any
  * user-facing change?" (causal attention with the mask reset at every EOD).
- * meta must come from thd_build_metadata with the tile sizes of
- * thd_preferred_tiles or thd_preferred_fwd_tiles and the current device.
+ * meta must come from thd_build_metadata (or thd_build_metadata_padded, or
+ * thd_build_packed_metadata) with the tile sizes of thd_preferred_tiles or
+ * thd_preferred_fwd_tiles and the current device.
  * softmax_scale >= 0 and finite; 0 selects 1/sqrt(d_qk). Supported (d_qk, d_v): (64,64), (128,128),
  * (192,128); Hq/Hkv <= 128. q, k, v, o, lse must be 16-byte aligned; k and v
  * must each be smaller than 4 GiB (THD_ERANGE otherwise). workspace (16-byte
@@ -349,7 +390,8 @@ int thd_attn_bwd_workspace(const thd_meta* meta, int32_t hq, int64_t* bytes);
  * "[Optim] FlashMask-4 Overlap support part 1 (NVSHMEM backend) - #166",
  * feature list: reduce-scatter in the backward) sums to their owners.
  * softmax_scale as for thd_attn_fwd (0 selects 1/sqrt(d_qk)); same head
- * dims, alignment and size limits; metadata with block_n = 64.
+ * dims, alignment and size limits; metadata with block_n = 64, not a pass
+ * plan nor a packed plan (THD_EMISMATCH).
  * Backward: dq, and this rank's partial dk, dv (all fp32, layouts above),
  * from the forward's lse and the upstream gradient d_o. dk and dv are written
  * in full (zeros for keys no local query sees). The softmax-gradient term

@@ -60,8 +60,11 @@ Packed forward plans (version 4; short-segment packing, a reading of the
 column-wise [start, end) key bounds per row of the FlashMask kernels named on
 "[Optim] FlashMask-4 Overlap support part 1 (NVSHMEM backend) - #166"). A
 (document, slot) whose chunk length is not a multiple of BT leaves one
-partial tile, its last. With key_cap = BN * (largest n_kv over all tiles),
-the partial tiles are taken in tile order and grouped greedily. A tile of
+partial tile, its last. With key_cap = BN * K, where K is the largest n_kv
+over all tiles, or min(K, kv_split) when the split rule above gives the
+plain tiles a kv_split > 0 for the plan's concurrency (a packed tile is never
+split, so it must not outlast the split parts), the partial tiles are taken
+in tile order and grouped greedily. A tile of
 document i adds keys add = kv_len - kv_len(prev) when the group's previous
 member is also of document i (its keys are then a prefix of this tile's) and
 add = kv_len otherwise; it joins the open group while the group's tokens plus
@@ -272,14 +275,17 @@ def pass_plan(seqlens, cp: int, rank: int, block_t: int, block_n: int, shards):
     return items, np.asarray(table, dtype=np.int32).reshape(-1, 4)
 
 
-def packed_plan(seqlens, cp: int, rank: int, block_t: int, block_n: int, real_lengths=None):
+def packed_plan(seqlens, cp: int, rank: int, block_t: int, block_n: int, real_lengths=None,
+                concurrency: int = 0):
     """(tiles, pack_rows, pack_keys) of a packed forward plan (module docstring)."""
     lengths = partition.validate(seqlens, cp, rank)
     tt = tiles(lengths, cp, rank, block_t, block_n)
     cu = partition.cu_seqlens(lengths)
     rowmap = partition.kv_row(lengths, cp)
     ends = doc_end(lengths, cp, real_lengths)
-    key_cap = block_n * max(int(x) for x in tt[:, 6])
+    longest = max(int(x) for x in tt[:, 6])
+    split = kv_split_for(tt, concurrency)
+    key_cap = block_n * (min(longest, split) if split > 0 else longest)
 
     def kv_len(t):
         return int(tt[t, 1]) + int(tt[t, 2]) - int(tt[t, 5])
@@ -337,7 +343,7 @@ def packed_forward_plan(seqlens, cp: int, rank: int, block_t: int, block_n: int,
                         concurrency: int, real_lengths=None) -> dict:
     """Every table of a packed forward plan: tiles, order, items, splits,
     pack_rows, pack_keys (order and items over the packed tile list)."""
-    tt, rows, keys = packed_plan(seqlens, cp, rank, block_t, block_n, real_lengths)
+    tt, rows, keys = packed_plan(seqlens, cp, rank, block_t, block_n, real_lengths, concurrency)
     items, splits = items_and_splits(tt, concurrency)
     return {"tiles": tt, "order": order(tt), "items": items, "splits": splits,
             "pack_rows": rows, "pack_keys": keys}

@@ -26,8 +26,8 @@ STATUS_NAMES = {
     -5: "THD_EMISMATCH", -6: "THD_EHIP", -7: "THD_ENOMEM", -8: "THD_EUNSUPPORTED",
 }
 FIELDS = {"q_global": 0, "kv_row": 1, "chunk_off": 2, "tiles": 3, "order": 4, "kvtiles": 5,
-          "items": 6, "splits": 7, "doc_end": 8}
-META_VERSION = 3
+          "items": 6, "splits": 7, "doc_end": 8, "pack_rows": 9, "pack_keys": 10}
+META_VERSION = 4
 
 
 class ThdError(RuntimeError):
@@ -52,6 +52,8 @@ class _Info(ctypes.Structure):
         ("device", ctypes.c_int32), ("cache_hit", ctypes.c_int32),
         ("is_pass", ctypes.c_int32), ("item_ints", ctypes.c_int32),
         ("shard_mask", ctypes.c_uint64),
+        ("n_packed_tiles", ctypes.c_int64), ("n_pack_rows", ctypes.c_int64),
+        ("n_pack_keys", ctypes.c_int64), ("is_packed", ctypes.c_int32), ("reserved", ctypes.c_int32),
     ]
 
 
@@ -71,6 +73,8 @@ def _load():
                                               ctypes.POINTER(p)]),
         "thd_pad_lengths": (ctypes.c_int, [pi32, i32, i32, pi32]),
         "thd_build_metadata_padded": (ctypes.c_int, [pi32, i32, i32, i32, i32, i32, i32, i32,
+                                                     ctypes.POINTER(p)]),
+        "thd_build_packed_metadata": (ctypes.c_int, [pi32, i32, i32, i32, i32, i32, i32, i32, i32,
                                                      ctypes.POINTER(p)]),
         "thd_meta_info": (ctypes.c_int, [p, ctypes.POINTER(_Info)]),
         "thd_meta_copy": (ctypes.c_int, [p, i32, pi32, i64]),
@@ -104,7 +108,7 @@ def _load():
 
 _lib = _load()
 EXPORTS = ("thd_last_error", "thd_plan_partition", "thd_build_metadata", "thd_pad_lengths",
-           "thd_build_metadata_padded", "thd_meta_info",
+           "thd_build_metadata_padded", "thd_build_packed_metadata", "thd_meta_info",
            "thd_meta_copy", "thd_meta_release", "thd_cache_stats", "thd_cache_clear",
            "thd_preferred_tiles", "thd_preferred_fwd_tiles", "thd_fwd_concurrency",
            "thd_attn_fwd_workspace", "thd_attn_fwd", "thd_attn_fwd_noalloc",
@@ -192,14 +196,15 @@ class Meta:
              "order": inf["n_tiles"], "kvtiles": inf["n_kvtiles"] * 8,
              "items": inf["n_items"] * inf["item_ints"],
              "splits": (inf["n_tiles"] if inf["is_pass"] else inf["n_splits"]) * 4,
-             "doc_end": inf["n_docs"]}[name]
+             "doc_end": inf["n_docs"], "pack_rows": inf["n_pack_rows"] * 4,
+             "pack_keys": inf["n_pack_keys"]}[name]
         out = np.empty(n, np.int32)
         _check(_lib.thd_meta_copy(self._h, FIELDS[name], _ptr32(out), n))
         if name in ("tiles", "kvtiles"):
             out = out.reshape(-1, 8)
         if name == "items":
             out = out.reshape(-1, inf["item_ints"])
-        if name == "splits":
+        if name in ("splits", "pack_rows"):
             out = out.reshape(-1, 4)
         return out
 
@@ -224,15 +229,23 @@ def pad_lengths(*, seqlens, cp: int) -> np.ndarray:
 
 
 def build_metadata(*, seqlens, cp: int, rank: int, block_t: int, block_n: int,
-                   concurrency: int = 0, device: int = -1, padded: bool = False) -> Meta:
+                   concurrency: int = 0, device: int = -1, padded: bool = False,
+                   packed: bool = False) -> Meta:
     """Build or fetch cached metadata; device >= 0 also uploads it there.
 
     concurrency: work items of one kv head the device runs at once (0 = never
     split a tile's key range). padded: seqlens are real lengths of any size;
     each document is stored padded to pad_lengths() tokens, real tokens first
-    (tensors use the padded layout; pad rows get O = 0 and LSE = +inf)."""
+    (tensors use the padded layout; pad rows get O = 0 and LSE = +inf).
+    packed: a forward-only plan whose short partial query tiles are packed
+    together (thd_build_packed_metadata)."""
     lens = _lengths(seqlens)
     h = ctypes.c_void_p()
+    if packed:
+        _check(_lib.thd_build_packed_metadata(_ptr32(lens), len(lens), cp, rank, block_t, block_n,
+                                              concurrency, int(bool(padded)), device,
+                                              ctypes.byref(h)))
+        return Meta(h)
     fn = _lib.thd_build_metadata_padded if padded else _lib.thd_build_metadata
     _check(fn(_ptr32(lens), len(lens), cp, rank, block_t, block_n, concurrency, device,
               ctypes.byref(h)))
@@ -300,10 +313,13 @@ def device_concurrency(device: int, hkv: int, block_n: int = 64) -> int:
 
 def device_metadata(*, seqlens, cp: int, rank: int, hq: int, hkv: int, d_qk: int, d_v: int,
                     device: int, concurrency: int | None = None, padded: bool = False,
-                    forward: bool = False) -> Meta:
+                    forward: bool = False, packed: bool = False) -> Meta:
     """Metadata on a device with the kernels' tile sizes. forward=True picks the
     forward's sizes for this batch (possibly 32-key tiles, which the backward
-    does not take); otherwise the sizes serve both directions."""
+    does not take); otherwise the sizes serve both directions. packed (with
+    forward=True): pack the short partial query tiles (forward only)."""
+    if packed and not forward:
+        raise ThdError(-1, "packed plans are forward-only: pass forward=True")
     if forward:
         bt, bn = preferred_fwd_tiles(seqlens=seqlens, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=d_qk,
                                      d_v=d_v, padded=padded)
@@ -312,7 +328,7 @@ def device_metadata(*, seqlens, cp: int, rank: int, hq: int, hkv: int, d_qk: int
     if concurrency is None:
         concurrency = device_concurrency(device, hkv, bn)
     return build_metadata(seqlens=seqlens, cp=cp, rank=rank, block_t=bt, block_n=bn,
-                          concurrency=concurrency, device=device, padded=padded)
+                          concurrency=concurrency, device=device, padded=padded, packed=packed)
 
 
 def _scratch(device, nbytes: int, stream):
@@ -358,7 +374,7 @@ def _qkv_shapes(q, k, v):
 
 def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=None, lse=None,
              out_f32=None, stream=None, meta: Meta | None = None, concurrency: int | None = None,
-             padded: bool = False):
+             padded: bool = False, packed: bool = False):
     """Forward attention for one rank. Returns (o bf16 [T_loc,Hq,dv], lse fp32 [T_loc,Hq]).
 
     q [T_loc, Hq, dqk], k [T, Hkv, dqk], v [T, Hkv, dv]: bf16 CUDA tensors,
@@ -366,7 +382,9 @@ def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=No
     1/sqrt(dqk). out_f32 (optional fp32 [T_loc, Hq, dv] tensor) also receives O
     in fp32, computed with split probabilities: pass it to attn_bwd as o_f32.
     padded: seqlens are real lengths and the tensors use the padded layout
-    (see build_metadata); pad rows get O = 0 and LSE = +inf.
+    (see build_metadata); pad rows get O = 0 and LSE = +inf. packed: pack the
+    short partial query tiles of several documents into shared tiles (the same
+    attention with fewer workgroups; see build_metadata).
     """
     torch = _torch()
     hq, hkv, d_qk, d_v = _qkv_shapes(q, k, v)
@@ -374,7 +392,7 @@ def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=No
     if meta is None:
         meta = device_metadata(seqlens=seqlens, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=d_qk,
                                d_v=d_v, device=dev.index, concurrency=concurrency,
-                               padded=padded, forward=True)
+                               padded=padded, forward=True, packed=packed)
     inf = meta._cached_info()
     t_loc, total = inf["local_tokens"], inf["total_tokens"]
     _need("q", q, torch.bfloat16, (t_loc, hq, d_qk), dev)

@@ -32,7 +32,14 @@ struct Plan {
   // holds one [tile, first part slot, parts, 0] record per tile.
   bool pass = false;
   uint64_t shard_mask = 0;
+  // A packed plan (short-segment packing) also lists packed tiles
+  // (q_local_start = -1): their rows in pack_rows [local row, first slot, last
+  // slot, real] and their key slots' gathered rows in pack_keys. It has no
+  // backward key tiles.
+  bool packed = false;
+  int64_t n_packed = 0;
   std::vector<int32_t> q_global, kv_row, chunk_off, tiles, order, kvtiles, items, splits, doc_end;
+  std::vector<int32_t> pack_rows, pack_keys;
   int item_ints() const { return pass ? 8 : 4; }
 };
 
@@ -45,9 +52,12 @@ void plan_partition(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t 
 
 // Builds the full plan (partition maps + tile tables). real_lengths (may be
 // null: no padding) gives each document's real tokens, 1 <= R_i <= L_i.
+// packed: group the partial tiles of consecutive documents into packed tiles
+// before the order and the work items are formed (see pack_partial_tiles).
 std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t cp,
                                  int32_t rank, int32_t block_t, int32_t block_n,
-                                 int32_t concurrency, const int32_t* real_lengths);
+                                 int32_t concurrency, const int32_t* real_lengths,
+                                 bool packed = false);
 
 // The plan of one forward pass over the keys held by the source ranks in
 // shard_mask (bit s = rank s's shard): same tiles, items over maximal runs of
@@ -68,6 +78,8 @@ struct DeviceMeta {
   const int32_t* items = nullptr;
   const int32_t* splits = nullptr;
   const int32_t* doc_end = nullptr;
+  const int32_t* pack_rows = nullptr;
+  const int32_t* pack_keys = nullptr;
 };
 
 struct MetaEntry {
@@ -117,6 +129,11 @@ struct FwdParams {
   int32_t ranged, pass_flags;
   float* state;
   int64_t local;
+  // Packed plans only: rows [local row, first slot, last slot, real] of the
+  // packed tiles, and each key slot's gathered row.
+  int32_t packed;
+  const int32_t* pack_rows;
+  const int32_t* pack_keys;
 };
 
 #if defined(__HIPCC__)

@@ -64,18 +64,20 @@ struct DeviceScope {
 void upload(MetaEntry& e, int device) {
   const Plan& p = *e.plan;
   DeviceScope scope(device);
-  const std::vector<int32_t>* parts[8] = {&p.kv_row, &p.tiles, &p.order, &p.kvtiles,
-                                          &p.q_global, &p.items, &p.splits, &p.doc_end};
-  size_t offs[8];
+  constexpr int kParts = 10;
+  const std::vector<int32_t>* parts[kParts] = {&p.kv_row,  &p.tiles,  &p.order,   &p.kvtiles,
+                                               &p.q_global, &p.items, &p.splits,  &p.doc_end,
+                                               &p.pack_rows, &p.pack_keys};
+  size_t offs[kParts];
   size_t bytes = 0;
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < kParts; ++i) {
     offs[i] = bytes;
     bytes += (parts[i]->size() * sizeof(int32_t) + 255) / 256 * 256;
   }
   void* base = nullptr;
   check_hip(hipMalloc(&base, bytes == 0 ? 256 : bytes), "hipMalloc(metadata)");
   std::vector<char> staging(bytes);
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < kParts; ++i)
     if (!parts[i]->empty())
       std::memcpy(staging.data() + offs[i], parts[i]->data(), parts[i]->size() * sizeof(int32_t));
   const hipError_t err = hipMemcpy(base, staging.data(), bytes, hipMemcpyHostToDevice);
@@ -94,6 +96,8 @@ void upload(MetaEntry& e, int device) {
   e.dev.items = reinterpret_cast<const int32_t*>(b + offs[5]);
   e.dev.splits = reinterpret_cast<const int32_t*>(b + offs[6]);
   e.dev.doc_end = reinterpret_cast<const int32_t*>(b + offs[7]);
+  e.dev.pack_rows = reinterpret_cast<const int32_t*>(b + offs[8]);
+  e.dev.pack_keys = reinterpret_cast<const int32_t*>(b + offs[9]);
 }
 
 // Least-recently-used cache of metadata entries. Entries still referenced by a
@@ -115,11 +119,11 @@ Cache& cache() {
 
 std::string make_key(const int32_t* seqlens, const int32_t* real, int32_t n_docs, int32_t cp,
                      int32_t rank, int32_t block_t, int32_t block_n, int32_t concurrency,
-                     int32_t device, bool pass, uint64_t shard_mask) {
-  const int32_t head[12] = {THD_META_VERSION, cp,     rank,    block_t,
+                     int32_t device, bool pass, uint64_t shard_mask, bool packed) {
+  const int32_t head[13] = {THD_META_VERSION, cp,     rank,    block_t,
                             block_n,          concurrency, device, n_docs,
                             real != nullptr ? 1 : 0, pass ? 1 : 0, int32_t(shard_mask & 0xffffffffu),
-                            int32_t(shard_mask >> 32)};
+                            int32_t(shard_mask >> 32), packed ? 1 : 0};
   const size_t n = size_t(n_docs) * sizeof(int32_t);
   std::string key(sizeof(head) + (real != nullptr ? 2 : 1) * n, '\0');
   std::memcpy(&key[0], head, sizeof(head));
@@ -207,11 +211,12 @@ void pad_lengths(const int32_t* real, int32_t n_docs, int32_t cp, int32_t* padde
   }
 }
 
-// Shared by thd_build_metadata (real = NULL) and thd_build_metadata_padded.
+// Shared by thd_build_metadata (real = NULL), thd_build_metadata_padded,
+// thd_build_pass_metadata (pass) and thd_build_packed_metadata (packed).
 void build_metadata_impl(const int32_t* seqlens, const int32_t* real, int32_t n_docs, int32_t cp,
                          int32_t rank, int32_t block_t, int32_t block_n, int32_t concurrency,
                          int32_t device, thd_meta** out, bool pass = false,
-                         uint64_t shard_mask = 0) {
+                         uint64_t shard_mask = 0, bool packed = false) {
   if (out == nullptr) fail(THD_EINVAL, "out is NULL");
   *out = nullptr;
   validate_partition(seqlens, n_docs, cp, rank);
@@ -223,7 +228,7 @@ void build_metadata_impl(const int32_t* seqlens, const int32_t* real, int32_t n_
     if (device >= count) fail(THD_EINVAL, "no such device " + std::to_string(device));
   }
   const std::string key = make_key(seqlens, real, n_docs, cp, rank, block_t, block_n,
-                                   concurrency, device, pass, shard_mask);
+                                   concurrency, device, pass, shard_mask, packed);
   Cache& c = cache();
   std::lock_guard<std::mutex> lock(c.mu);
   auto hit = c.map.find(key);
@@ -237,7 +242,8 @@ void build_metadata_impl(const int32_t* seqlens, const int32_t* real, int32_t n_
     ++c.misses;
     auto e = std::make_shared<MetaEntry>();
     e->plan = pass ? build_pass_plan(seqlens, n_docs, cp, rank, block_t, block_n, shard_mask)
-                   : build_plan(seqlens, n_docs, cp, rank, block_t, block_n, concurrency, real);
+                   : build_plan(seqlens, n_docs, cp, rank, block_t, block_n, concurrency, real,
+                                packed);
     if (device >= 0) {
       upload(*e, device);
       ++c.uploads;
@@ -315,6 +321,26 @@ int thd_build_metadata_padded(const int32_t* real_lengths, int32_t n_docs, int32
   });
 }
 
+int thd_build_packed_metadata(const int32_t* lengths, int32_t n_docs, int32_t cp, int32_t rank,
+                              int32_t block_t, int32_t block_n, int32_t concurrency,
+                              int32_t padded, int32_t device, thd_meta** out) {
+  return guarded([&] {
+    if (out == nullptr) fail(THD_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (padded != 0 && padded != 1) fail(THD_EINVAL, "padded must be 0 or 1");
+    if (padded == 0) {
+      build_metadata_impl(lengths, nullptr, n_docs, cp, rank, block_t, block_n, concurrency,
+                          device, out, false, 0, true);
+      return;
+    }
+    if (n_docs < 1) fail(THD_EINVAL, "n_docs must be >= 1");
+    std::vector<int32_t> stored(n_docs);
+    pad_lengths(lengths, n_docs, cp, stored.data());
+    build_metadata_impl(stored.data(), lengths, n_docs, cp, rank, block_t, block_n, concurrency,
+                        device, out, false, 0, true);
+  });
+}
+
 int thd_meta_info(const thd_meta* meta, thd_meta_info_t* info) {
   return guarded([&] {
     const MetaEntry& e = entry_of(meta);
@@ -343,6 +369,10 @@ int thd_meta_info(const thd_meta* meta, thd_meta_info_t* info) {
     info->is_pass = p.pass ? 1 : 0;
     info->item_ints = p.item_ints();
     info->shard_mask = p.shard_mask;
+    info->is_packed = p.packed ? 1 : 0;
+    info->n_packed_tiles = p.n_packed;
+    info->n_pack_rows = int64_t(p.pack_rows.size() / 4);
+    info->n_pack_keys = int64_t(p.pack_keys.size());
   });
 }
 
@@ -360,6 +390,8 @@ int thd_meta_copy(const thd_meta* meta, int32_t field, int32_t* dst, int64_t cou
       case THD_FIELD_ITEMS: src = &p.items; break;
       case THD_FIELD_SPLITS: src = &p.splits; break;
       case THD_FIELD_DOC_END: src = &p.doc_end; break;
+      case THD_FIELD_PACK_ROWS: src = &p.pack_rows; break;
+      case THD_FIELD_PACK_KEYS: src = &p.pack_keys; break;
       default: fail(THD_EINVAL, "unknown field " + std::to_string(field));
     }
     if (count != int64_t(src->size()))
@@ -545,6 +577,9 @@ void attn_fwd_impl(const thd_meta* meta, const void* q, const void* k, const voi
   fp.splits = d.splits;
   fp.kv_row = d.kv_row;
   fp.doc_end = d.doc_end;
+  fp.packed = p.packed ? 1 : 0;
+  fp.pack_rows = d.pack_rows;
+  fp.pack_keys = d.pack_keys;
   fp.n_items = int32_t(n_items);
   fp.n_splits = int32_t(p.splits.size() / 4);
   fp.hq = hq;
@@ -699,6 +734,9 @@ int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void*
     const int32_t group = hq / hkv;
     check_bwd_tiles(p, group);
     if (p.pass) fail(THD_EMISMATCH, "metadata is a pass plan, not the full key range");
+    if (p.packed)
+      fail(THD_EMISMATCH, "metadata is a packed plan, which is forward-only: build it with "
+                          "thd_build_metadata for the backward");
     check_ptr(q, "q", 16);
     check_ptr(k, "k", 16);
     check_ptr(v, "v", 16);

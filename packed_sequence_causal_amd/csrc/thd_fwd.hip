@@ -57,6 +57,7 @@ typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef int i32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) void lds_void;
@@ -142,7 +143,12 @@ constexpr int kFwdOccupancy = BN == kBlockNShort ? 3 : 2;
 
 // RANGED: items of a pass plan (all-gather overlap), 8 ints with an absolute
 // key range [first key, end key) per item, always written as a part.
-template <int DQK, int DV, bool EXACT, int BN_, bool RANGED = false>
+// PACKED: a packed plan's items, some of whose tiles are packed tiles (rows of
+// several documents; short-segment packing): such a tile's rows, their key
+// windows and its key slots come from pack_rows / pack_keys, every KV tile
+// takes the two-sided window compare, and a wave skips the KV tiles its rows'
+// windows do not reach.
+template <int DQK, int DV, bool EXACT, int BN_, bool RANGED = false, bool PACKED = false>
 __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kernel(FwdParams p) {
   using S = FwdShape<DQK, DV, BN_>;
   constexpr int BN = S::BN;
@@ -170,23 +176,31 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
   const int kv_end = RANGED ? item[4] : item[2];
   const int part = item[3];
   const int32_t* td = p.tiles + size_t(tile) * 8;
+  // A packed tile's td[1] is its first row in pack_rows and td[5] its first
+  // key slot; its slots are numbered from 0 and fill td[6] whole KV tiles.
+  const bool packed_tile = PACKED && td[0] < 0;
   const int q_local0 = td[0];
   const int q_glob0 = td[1];
   const int n_rows = td[2];
   // KV tiles start at the document's first key (a pass plan's item: at its
   // run's first key); keys from key_hi on are seen by no row of the item.
-  const int kv_start = RANGED ? item[1] : td[5];
+  const int kv_start = RANGED ? item[1] : (packed_tile ? 0 : td[5]);
   const int n_full = RANGED ? item[5] : td[7];
-  const int key_hi = RANGED ? item[2] : q_glob0 + n_rows;
+  const int key_hi = RANGED ? item[2] : (packed_tile ? td[6] * BN : q_glob0 + n_rows);
   // Rows at or past the document's last real token are padding: written as
-  // O = 0, LSE = +inf (tokens are in position order within a tile).
-  const int n_real = min(max(p.doc_end[td[3]] - q_glob0, 0), n_rows);
+  // O = 0, LSE = +inf (tokens are in position order within a plain tile; a
+  // packed row carries its own flag).
+  const int n_real = packed_tile ? 0 : min(max(p.doc_end[td[3]] - q_glob0, 0), n_rows);
   const int key_last = key_hi - 1;
 
   // Row block rb of this wave holds rows 32 * (RB * wave + rb) + lane % 32.
   const int G = p.group;
-  int tok[RB], head[RB], qpos[RB];
-  bool valid[RB], rb_active[RB];
+  // qpos: the last key (slot) a row sees. Packed plans only: qlo, the first;
+  // for rows of a packed tile, pk_row and pk_real hold its local query row
+  // and whether it is real (other kernels derive both from the token when
+  // they store, which keeps them out of registers during the tile loop).
+  int tok[RB], head[RB], qpos[RB], qlo[RB], pk_row[RB];
+  bool valid[RB], rb_active[RB], pk_real[RB];
 #pragma unroll
   for (int rb = 0; rb < RB; ++rb) {
     const int row0 = 32 * (RB * wave + rb);
@@ -196,6 +210,19 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
     valid[rb] = tok[rb] < n_rows;
     // The causal compare also ends a pass item's range at key_hi.
     qpos[rb] = valid[rb] ? (RANGED ? min(q_glob0 + tok[rb], key_last) : q_glob0 + tok[rb]) : INT_MAX;
+    qlo[rb] = 0;
+    pk_row[rb] = q_local0 + tok[rb];
+    pk_real[rb] = tok[rb] < n_real;
+    if constexpr (PACKED) {
+      if (packed_tile) {
+        const i32x4 pr = valid[rb] ? *reinterpret_cast<const i32x4*>(p.pack_rows + 4 * size_t(q_glob0 + tok[rb]))
+                                   : i32x4{0, 0, INT_MAX, 0};
+        pk_row[rb] = pr[0];
+        qlo[rb] = pr[1];
+        qpos[rb] = pr[2];
+        pk_real[rb] = pr[3] != 0;
+      }
+    }
     rb_active[rb] = row0 / G < n_rows;          // wave-uniform
   }
   const bool wave_active = rb_active[0];
@@ -203,18 +230,26 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
   const __bf16* __restrict__ qp = static_cast<const __bf16*>(p.q);
   const char* __restrict__ kb = static_cast<const char*>(p.k);
   const char* __restrict__ vb = static_cast<const char*>(p.v);
-  const int32_t* __restrict__ kv_row = p.kv_row;
+  const int32_t* __restrict__ kv_row = packed_tile ? p.pack_keys + td[5] : p.kv_row;
   const int hkv = p.hkv;
 
   // Q^T operand: lane holds Q[row][16*st + 8*half .. +7] for each k-step.
+  // A packed tile's rows are known only once pack_rows has arrived, so its Q
+  // loads go out after the first KV tile's copies (its key rows are fetched
+  // alongside pack_rows): the first tile then waits on one dependent load,
+  // as in a plain tile, instead of two.
   bf16x8 qf[RB][S::KSTEPS];
+  auto load_q = [&]() __attribute__((always_inline)) {
 #pragma unroll
-  for (int rb = 0; rb < RB; ++rb) {
-    const __bf16* qrow = qp + (size_t(q_local0 + tok[rb]) * p.hq + head[rb]) * DQK + 8 * half;
+    for (int rb = 0; rb < RB; ++rb) {
+      const int qrow = PACKED ? pk_row[rb] : q_local0 + tok[rb];
+      const __bf16* qsrc = qp + (size_t(qrow) * p.hq + head[rb]) * DQK + 8 * half;
 #pragma unroll
-    for (int st = 0; st < S::KSTEPS; ++st)
-      qf[rb][st] = valid[rb] ? *reinterpret_cast<const bf16x8*>(qrow + 16 * st) : bf16x8{};
-  }
+      for (int st = 0; st < S::KSTEPS; ++st)
+        qf[rb][st] = valid[rb] ? *reinterpret_cast<const bf16x8*>(qsrc + 16 * st) : bf16x8{};
+    }
+  };
+  if constexpr (!PACKED) load_q();
 
   // Loader geometry: load i of this wave fills LDS bytes [1 KB * gi, +1 KB) of
   // the K (or V) tile, gi = wave * IPW + i; lane l writes slot q = 64 gi + l,
@@ -277,7 +312,10 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
   for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
     for (int b = 0; b < S::DVB; ++b) acc[rb][b] = f32x16{};
-    m_run[rb] = -INFINITY;
+    // A packed row can meet KV tiles it sees nothing of before its first
+    // visible one: a finite start keeps exp2(s - m) at 0 for those (-inf - m),
+    // where -inf - (-inf) would be NaN.
+    m_run[rb] = PACKED ? -__FLT_MAX__ : -INFINITY;
     l_run[rb] = 0.0f;
   }
   const float c2 = p.scale_log2;
@@ -286,6 +324,19 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
   fetch_rows(kv_begin, rows_cur);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   issue_tile(smem0, rows_cur);
+  // Packed tiles: the slot window of the wave's rows. Both ends of the rows'
+  // windows grow along the rows, so it runs from the first row's first slot
+  // to the last valid row's last slot; KV tiles outside it are skipped.
+  int w_lo = 0, w_hi = INT_MAX;
+  if constexpr (PACKED) {
+    static_assert(RB == 1, "the wave window reads one row block");
+    load_q();
+    if (packed_tile && wave_active) {
+      const int last = min(31, n_rows * G - 1 - 32 * wave);
+      w_lo = __builtin_amdgcn_readfirstlane(qlo[0]);
+      w_hi = __builtin_amdgcn_readfirstlane(__shfl(qpos[0], last));
+    }
+  }
   if (kv_begin + 1 < kv_end) fetch_rows(kv_begin + 1, rows_cur);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   __syncthreads();
@@ -295,7 +346,7 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
     if (j + 1 < kv_end) issue_tile(next, rows_cur);
     if (j + 2 < kv_end) fetch_rows(j + 2, rows_nxt);
 
-    if (wave_active) {
+    if (wave_active && (!PACKED || (j * BN <= w_hi && j * BN + BN - 1 >= w_lo))) {
       // S^T = K Q^T for keys [32*kb, 32*kb + 32) of the tile; each K fragment
       // read from LDS feeds every row block.
       f32x16 s[RB][S::KB];
@@ -359,19 +410,26 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
             // constant offsets, one compare and one select per element. It
             // pays where most tiles are masked (short documents, -2%); with
             // 64-key tiles the other form timed slightly faster.
+            // A packed row's window also has a first slot (lim_lo; <= 0, so
+            // no bound, outside packed tiles). One form for both kinds of
+            // tile: a branch between two copies costs the 32-key kernel 44
+            // more bytes of spills.
             const int lim = qpos[rb] - key0;
+            const int lim_lo = qlo[rb] - key0;
 #pragma unroll
             for (int kb2 = 0; kb2 < S::KB; ++kb2)
 #pragma unroll
-              for (int r = 0; r < 16; ++r)
-                if (32 * kb2 + 8 * (r >> 2) + (r & 3) > lim) s[rb][kb2][r] = -INFINITY;
+              for (int r = 0; r < 16; ++r) {
+                const int off = 32 * kb2 + 8 * (r >> 2) + (r & 3);
+                if (off > lim || (PACKED && off < lim_lo)) s[rb][kb2][r] = -INFINITY;
+              }
           } else {
 #pragma unroll
             for (int kb2 = 0; kb2 < S::KB; ++kb2)
 #pragma unroll
               for (int r = 0; r < 16; ++r) {
                 const int key = key0 + 32 * kb2 + 8 * (r >> 2) + (r & 3);
-                if (key > qpos[rb]) s[rb][kb2][r] = -INFINITY;
+                if (key > qpos[rb] || (PACKED && key < qlo[rb])) s[rb][kb2][r] = -INFINITY;
               }
           }
         }
@@ -529,9 +587,10 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
   // wave writes its 32 rows into its own part of the ring (free once the last
   // tile's barrier has passed), 16-byte chunks XOR-swizzled by row, then
   // stores whole rows, 16 bytes per lane.
-  const bool real = tok[0] < n_real;   // pad rows get O = 0
   char* region = (wave < 2 ? smem0 : smem1) + (wave & 1) * (32 * S::VROWB);
-  const size_t orow_idx = size_t(q_local0 + tok[0]) * p.hq + head[0];
+  const int qrow = PACKED ? pk_row[0] : q_local0 + tok[0];
+  const bool real = PACKED ? pk_real[0] : tok[0] < n_real;
+  const size_t orow_idx = size_t(qrow) * p.hq + head[0];
 #pragma unroll
   for (int b = 0; b < S::DVB; ++b)
 #pragma unroll
@@ -540,7 +599,7 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
       bf16x4 out;
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        o4[e] = real ? acc[0][b][4 * g + e] * inv : 0.0f;
+        o4[e] = real ? acc[0][b][4 * g + e] * inv : 0.0f;   // pad rows get O = 0
         out[e] = static_cast<__bf16>(o4[e]);
       }
       const int chunk = (4 * b + g) ^ (lrow & (S::VCPR - 1));
@@ -560,8 +619,9 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
     const bf16x8 v8 = *reinterpret_cast<const bf16x8*>(region + r * S::VROWB + ((c ^ (r & (S::VCPR - 1))) << 4));
     const int tok_r = __shfl(tok[0], r);
     const int head_r = __shfl(head[0], r);
+    const int qrow_r = PACKED ? __shfl(qrow, r) : q_local0 + tok_r;
     if (tok_r < n_rows)
-      *reinterpret_cast<bf16x8*>(obase + (size_t(q_local0 + tok_r) * p.hq + head_r) * DV + 8 * c) = v8;
+      *reinterpret_cast<bf16x8*>(obase + (size_t(qrow_r) * p.hq + head_r) * DV + 8 * c) = v8;
   }
 }
 
@@ -718,7 +778,12 @@ template <int DQK, int DV, int BN>
 int launch(const FwdParams& p, void* stream) {
   hipStream_t st = static_cast<hipStream_t>(stream);
   const dim3 grid(unsigned(int64_t(p.n_items) * p.hkv));
-  if (p.o_f32 != nullptr) {
+  if (p.packed) {
+    if (p.o_f32 != nullptr)
+      hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV, true, BN, false, true>), grid, dim3(kFwdThreads), 0, st, p);
+    else
+      hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV, false, BN, false, true>), grid, dim3(kFwdThreads), 0, st, p);
+  } else if (p.o_f32 != nullptr) {
     hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV, true, BN>), grid, dim3(kFwdThreads), 0, st, p);
   } else {
     hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV, false, BN>), grid, dim3(kFwdThreads), 0, st, p);

@@ -16,6 +16,13 @@
 // position, and only the tiles past the first row's position need the causal
 // compare. The arrays are built in one pass with closed forms. The longest
 // tiles' key ranges may be split into several forward work items (below).
+//
+// Packed plans (short-segment packing, after the per-row [start, end) key
+// bounds of the FlashMask kernels on "[Optim] FlashMask-4 Overlap support
+// part 1 (NVSHMEM backend) - #166"): the last, partial tile of each chunk is
+// grouped with its neighbours' into one tile of up to block_t rows, whose key
+// slots hold the documents' keys one document after the other and whose rows
+// each see one window of slots.
 #include <algorithm>
 #include <cstring>
 #include <numeric>
@@ -72,9 +79,98 @@ void plan_partition(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t 
   }
 }
 
+namespace {
+
+// Replaces the partial tiles of p.tiles (n_rows < block_t) by packed tiles.
+// The partial tiles are taken in tile order and grouped greedily: a tile joins
+// the open group while the group stays within block_t rows and within
+// block_n * K key slots, K = max_kv_tiles, or the plain tiles' kv_split when
+// that is positive and smaller (a packed tile is never split, so it must not
+// outlast the longest plain tile nor the split parts); a tile of the same
+// document as the group's previous member adds only the keys past that
+// member's (its keys extend the member's). Groups of
+// one tile stay plain. Plain tiles keep their tile order and the packed tiles
+// follow in group order as [-1, first pack row, rows, -1, -1, first pack key,
+// n_kv, 0]. Each packed row gets [local row, first slot, last slot, real]; a
+// document's keys cu_i .. cu_i + K_i - 1 take consecutive slots from the
+// document's base, K_i the key count of its last member, and row g of the
+// document sees slots base .. base + g - cu_i. The slots are padded to whole
+// KV tiles with the last slot's row, which no row sees.
+void pack_partial_tiles(Plan& p) {
+  const int64_t n = int64_t(p.tiles.size() / 8);
+  auto rec = [&](int64_t t) { return &p.tiles[size_t(t) * 8]; };
+  auto kv_len = [&](int64_t t) { return int64_t(rec(t)[1]) + rec(t)[2] - rec(t)[5]; };
+  int64_t cap_tiles = p.max_kv_tiles;
+  if (p.concurrency > 0 && n < 2 * int64_t(p.concurrency)) {
+    int64_t total_kv = 0;
+    for (int64_t t = 0; t < n; ++t) total_kv += rec(t)[6];
+    const int64_t split = std::max<int64_t>((total_kv + p.concurrency - 1) / p.concurrency, 8);
+    cap_tiles = std::min(cap_tiles, split);
+  }
+  const int64_t key_cap = int64_t(p.block_n) * cap_tiles;
+  std::vector<std::vector<int64_t>> groups;
+  std::vector<int64_t> group;
+  int64_t g_rows = 0, g_keys = 0;
+  for (int64_t t = 0; t < n; ++t) {
+    const int64_t n_rows = rec(t)[2];
+    if (n_rows == p.block_t) continue;
+    const bool same_doc = !group.empty() && rec(group.back())[3] == rec(t)[3];
+    const int64_t add = kv_len(t) - (same_doc ? kv_len(group.back()) : 0);
+    if (!group.empty() && g_rows + n_rows <= p.block_t && g_keys + add <= key_cap) {
+      group.push_back(t);
+      g_rows += n_rows;
+      g_keys += add;
+      continue;
+    }
+    if (!group.empty()) groups.push_back(std::move(group));
+    group.assign(1, t);
+    g_rows = n_rows;
+    g_keys = kv_len(t);
+  }
+  if (!group.empty()) groups.push_back(std::move(group));
+
+  std::vector<char> in_pack(size_t(n), 0);
+  for (const auto& g : groups)
+    if (g.size() > 1)
+      for (int64_t t : g) in_pack[size_t(t)] = 1;
+  std::vector<int32_t> out;
+  out.reserve(p.tiles.size());
+  for (int64_t t = 0; t < n; ++t)
+    if (!in_pack[size_t(t)]) out.insert(out.end(), rec(t), rec(t) + 8);
+  for (const auto& g : groups) {
+    if (g.size() < 2) continue;
+    const int64_t row0 = int64_t(p.pack_rows.size() / 4), key0 = int64_t(p.pack_keys.size());
+    int64_t base = 0;
+    for (size_t m = 0; m < g.size(); ++m) {
+      const int32_t* r = rec(g[m]);
+      if (m > 0 && rec(g[m - 1])[3] != r[3]) base += kv_len(g[m - 1]);
+      const int64_t q_local = r[0], q_glob = r[1], n_rows = r[2], doc = r[3], cu = r[5];
+      for (int64_t o = 0; o < n_rows; ++o) {
+        const int64_t pos = q_glob + o;
+        const int32_t prow[4] = {int32_t(q_local + o), int32_t(base), int32_t(base + pos - cu),
+                                 pos < p.doc_end[size_t(doc)] ? 1 : 0};
+        p.pack_rows.insert(p.pack_rows.end(), prow, prow + 4);
+      }
+      // The document's keys, once its last member (which sees the most) is reached.
+      if (m + 1 == g.size() || rec(g[m + 1])[3] != r[3])
+        p.pack_keys.insert(p.pack_keys.end(), p.kv_row.begin() + cu, p.kv_row.begin() + cu + kv_len(g[m]));
+    }
+    const int64_t slots = int64_t(p.pack_keys.size()) - key0;
+    const int64_t n_kv = (slots + p.block_n - 1) / p.block_n;
+    p.pack_keys.resize(size_t(key0 + n_kv * p.block_n), p.pack_keys.back());
+    const int32_t prec[8] = {-1, int32_t(row0), int32_t(int64_t(p.pack_rows.size() / 4) - row0),
+                             -1, -1, int32_t(key0), int32_t(n_kv), 0};
+    out.insert(out.end(), prec, prec + 8);
+    ++p.n_packed;
+  }
+  p.tiles.swap(out);
+}
+
+}  // namespace
+
 std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t cp,
                                  int32_t rank, int32_t block_t, int32_t block_n,
-                                 int32_t concurrency, const int32_t* real_lengths) {
+                                 int32_t concurrency, const int32_t* real_lengths, bool packed) {
   const int64_t total = validate_partition(seqlens, n_docs, cp, rank);
   if (real_lengths != nullptr)
     for (int32_t i = 0; i < n_docs; ++i)
@@ -138,6 +234,10 @@ std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t
     doc_end_tile[i] = int64_t(p.tiles.size() / 8);
     cu += seqlens[i];
   }
+  if (packed) {
+    p.packed = true;
+    pack_partial_tiles(p);
+  }
   const int64_t n_tiles = int64_t(p.tiles.size() / 8);
 
   // Largest-first order: stable sort by KV-tile count, descending.
@@ -151,9 +251,10 @@ std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t
   // seeing a key tile form a suffix of the document's tiles, found by one
   // forward walk because tile end positions increase within a document; keys
   // past offset (2cp-r)*c_i are seen by no local query (the rank's later chunk
-  // is 2cp-1-r), so their tiles get an empty range.
+  // is 2cp-1-r), so their tiles get an empty range. (Packed plans are
+  // forward-only and have none.)
   cu = 0;
-  for (int32_t i = 0; i < n_docs; ++i) {
+  for (int32_t i = 0; i < n_docs && !p.packed; ++i) {
     const int64_t len = seqlens[i];
     int64_t qb = doc_first_tile[i];
     for (int64_t j = 0; j * block_n < len; ++j) {

@@ -450,3 +450,67 @@ def test_pass_metadata_errors():
                                  None, 0, None) == -1
     n = ctypes.c_int64()
     assert lib.thd_attn_fwd_pass_workspace(m.handle, 32, 8, 128, ctypes.byref(n), None) == -5
+
+
+def _compare_packed(lengths, cp, rank, bt, bn, concurrency, real=None):
+    m = thd.build_metadata(seqlens=real if real is not None else lengths, cp=cp, rank=rank,
+                           block_t=bt, block_n=bn, concurrency=concurrency,
+                           padded=real is not None, packed=True)
+    info = m.info()
+    want = ometa.packed_forward_plan(lengths, cp, rank, bt, bn, concurrency, real_lengths=real)
+    assert info["is_packed"] == 1 and info["is_pass"] == 0 and info["n_kvtiles"] == 0
+    assert info["n_packed_tiles"] == int((want["tiles"][:, 0] < 0).sum())
+    for name in ("tiles", "order", "items", "splits", "pack_rows", "pack_keys"):
+        got, ref = m.field(name), want[name]
+        assert got.size == ref.size and np.array_equal(got.reshape(-1), ref.reshape(-1)), name
+    return m
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_packed_plans_match_oracle_bit_for_bit(seed):
+    rng = np.random.default_rng(700 + seed)
+    cp = int(rng.choice([1, 2, 3, 4, 8]))
+    rank = int(rng.integers(0, cp))
+    real = [int(x) for x in rng.integers(1, 60 * cp, size=int(rng.integers(1, 12)))]
+    bt = int(rng.choice([2, 4, 8, 16, 32]))
+    bn = int(rng.choice([32, 64]))
+    concurrency = int(rng.choice([0, 2, 8]))
+    lengths = opart.pad_lengths(real, cp)
+    _compare_packed(lengths, cp, rank, bt, bn, concurrency)
+    _compare_packed(lengths, cp, rank, bt, bn, concurrency, real=real)
+
+
+@pytest.mark.parametrize("name", ["tiny", "gqa_mid", "mla", "short", "fwdbwd"])
+def test_packed_plans_of_the_workloads_match_oracle(name):
+    w = workloads.BY_NAME[name]
+    lengths = workloads.draw_lengths(w, np.random.default_rng(w.index))
+    g = w.hq // w.hkv
+    _compare_packed(lengths, w.cp, w.rank, 128 // g, 32 if w.d_qk <= 128 else 64, 0)
+
+
+def test_packed_metadata_errors_and_refusals():
+    lib = thd._lib
+    h = ctypes.c_void_p()
+    lens = np.asarray([8, 16], np.int32)
+    assert lib.thd_build_packed_metadata(thd._ptr32(lens), 2, 2, 0, 4, 64, 0, 2, -1,
+                                         ctypes.byref(h)) == -1
+    assert b"padded" in lib.thd_last_error()
+    with pytest.raises(thd.ThdError) as err:
+        thd.build_metadata(seqlens=[6], cp=2, rank=0, block_t=4, block_n=64, packed=True)
+    assert err.value.status == "THD_ENOTDIV"
+    # the packed flag is part of the cache key
+    plain = thd.build_metadata(seqlens=[8, 16, 8], cp=2, rank=0, block_t=4, block_n=64)
+    packed = thd.build_metadata(seqlens=[8, 16, 8], cp=2, rank=0, block_t=4, block_n=64,
+                                packed=True)
+    assert plain.info()["is_packed"] == 0 and packed.info()["is_packed"] == 1
+    assert packed.info()["n_packed_tiles"] > 0
+    # the backward refuses a packed plan before touching any pointer
+    buf = ctypes.create_string_buffer(1 << 16)
+    ptr = (ctypes.addressof(buf) + 15) // 16 * 16
+    mp = thd.build_metadata(seqlens=[256, 64], cp=1, rank=0, block_t=32, block_n=64, packed=True)
+    assert lib.thd_attn_bwd(mp.handle, ptr, ptr, ptr, ptr, None, ptr, ptr, ptr, ptr, 32, 8, 128,
+                            128, 0.0, ptr, 1 << 16, None) == -5
+    assert b"packed" in lib.thd_last_error()
+    with pytest.raises(thd.ThdError):
+        thd.device_metadata(seqlens=[256], cp=1, rank=0, hq=32, hkv=8, d_qk=128, d_v=128,
+                            device=0, packed=True)

@@ -157,3 +157,22 @@ def test_packed_forward_plan_items_cover_every_tile_once():
     assert set(cover) == want and all(c == 1 for c in cover.values())
     for tile, *_ in plan["splits"].tolist():
         assert int(tt[tile, 0]) >= 0   # packed tiles (n_full = 0) are never split
+
+
+@pytest.mark.parametrize("concurrency", [20, 50, 100])
+def test_packed_tiles_never_outlast_the_split_parts(concurrency):
+    """With a concurrency that splits the plain tiles (fewer than 2C tiles), a
+    packed tile (never split itself) holds at most kv_split KV tiles; the
+    packing still gives every row its causal keys (checked above)."""
+    lengths = [16, 24, 8, 40, 16, 8, 32, 200, 8, 24]
+    cp, rank, bt, bn = 2, 0, 8, 4
+    plain = metadata.tiles(lengths, cp, rank, bt, bn)
+    split = metadata.kv_split_for(plain, concurrency)
+    assert split > 0
+    cap = min(int(plain[:, 6].max()), split)
+    tt, rows, _ = metadata.packed_plan(lengths, cp, rank, bt, bn, concurrency=concurrency)
+    packed = tt[tt[:, 0] < 0]
+    assert packed.shape[0] > 0 and int(packed[:, 6].max()) <= cap
+    if concurrency == 100:
+        free, _, _ = metadata.packed_plan(lengths, cp, rank, bt, bn)
+        assert int(free[free[:, 0] < 0][:, 6].max()) > cap   # the cap binds here
