@@ -164,8 +164,8 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int half = lane >> 5;        // which 32-lane half
-  const int lrow = lane & 31;
+  int half = lane >> 5;        // which 32-lane half (recomputed for the epilogue)
+  int lrow = lane & 31;
 
   // Work item: KV tiles [kv_begin, kv_end) of one query tile (a whole tile
   // unless its key range is split), for kv head blockIdx.x % Hkv.
@@ -560,6 +560,20 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
 
   static_assert(RB == 1, "the epilogue stages one 32-row block per wave");
   if (!wave_active) return;
+  {
+    // Recompute the lane's row, token and head from an opaque copy of the
+    // lane id: otherwise the compiler keeps the address products it formed
+    // from them before the tile loop live across it, and spills them (12 to
+    // 28 bytes per lane in the 32-key and d_qk = 192 kernels).
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    half = ln >> 5;
+    lrow = ln & 31;
+    const int row = 32 * wave + lrow;
+    tok[0] = row / G;
+    head[0] = kvh * G + (row - tok[0] * G);
+    valid[0] = tok[0] < n_rows;
+  }
   const float l_tot = l_run[0] + __shfl_xor(l_run[0], 32);
   const float inv = 1.0f / l_tot;
   if (part >= 0) {
