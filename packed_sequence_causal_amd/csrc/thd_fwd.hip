@@ -305,6 +305,18 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
   const int tr_a = (lane & 15) >> 2;
   const int tr_c = lane & 3;
   const int tr_dv = 16 * ((lane >> 4) & 1) + 4 * tr_c;     // plus 32*b
+  // Offsets of those reads for 16-key step 0; a row's swizzle depends only on
+  // its index mod 16 (mod 8 for 8-chunk rows), so step t only adds 16 t rows,
+  // a constant that the reads take as their immediate offset.
+  int vt_off[2][S::DVB];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int b = 0; b < S::DVB; ++b) {
+      const int r = 4 * half + tr_a + 8 * h;
+      const int dv = 32 * b + tr_dv;
+      vt_off[h][b] = S::KBYTES + r * S::VROWB + (((dv >> 3) ^ swz<S::VCPR>(r)) << 4) + ((tr_c & 1) << 3);
+    }
 
   f32x16 acc[RB][S::DVB];
   float m_run[RB], l_run[RB];   // running max of scale*log2(e)*s, and this lane's share of the sum
@@ -347,6 +359,13 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
     if (j + 2 < kv_end) fetch_rows(j + 2, rows_nxt);
 
     if (wave_active && (!PACKED || (j * BN <= w_hi && j * BN + BN - 1 >= w_lo))) {
+      // Opaque to the compiler on every tile, so that it adds each read's
+      // constant in the read's immediate instead of keeping a register per
+      // (step, column block) live across the loop.
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int b = 0; b < S::DVB; ++b) asm volatile("" : "+v"(vt_off[h][b]));
       // S^T = K Q^T for keys [32*kb, 32*kb + 32) of the tile; each K fragment
       // read from LDS feeds every row block.
       f32x16 s[RB][S::KB];
@@ -499,8 +518,6 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
       // pairs are live at a time.
 #pragma unroll
       for (int t = 0; t < S::TS; ++t) {
-        const int r0 = 16 * t + 4 * half + tr_a;
-        const int r1 = r0 + 8;
         bf16x8 p_hi[RB], p_lo[RB];
         if constexpr (EXACT) {
 #pragma unroll
@@ -529,9 +546,8 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
         }
 #pragma unroll
         for (int b = 0; b < S::DVB; ++b) {
-          const int dv = 32 * b + tr_dv;
-          const int off0 = S::KBYTES + r0 * S::VROWB + (((dv >> 3) ^ swz<S::VCPR>(r0)) << 4) + ((tr_c & 1) << 3);
-          const int off1 = S::KBYTES + r1 * S::VROWB + (((dv >> 3) ^ swz<S::VCPR>(r1)) << 4) + ((tr_c & 1) << 3);
+          const int off0 = vt_off[0][b] + 16 * t * S::VROWB;
+          const int off1 = vt_off[1][b] + 16 * t * S::VROWB;
           const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + off0));
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(stage + off1));
           const bf16x8 a = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
