@@ -21,17 +21,20 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "-Wall", "-Werror", "-Wno-unused-command-line-argument",
           "-I" + os.path.join(ROOT, "include"), "-I" + CSRC]
-# NaNs are not data here (inputs are finite; masked scores are -inf), and with
-# the IEEE mode bit off v_max_f32 needs no canonicalising copy of each MFMA
-# result before the row-maximum tree (16 instructions per 64-key tile).
 DEVICE = ["-x", "hip", "--offload-arch=gfx950", "-Xclang", "-target-feature", "-Xclang",
-          "-packed-fp32-ops", "-Wno-unknown-warning-option", "-fno-honor-nans",
-          "-mno-amdgpu-ieee"]
+          "-packed-fp32-ops", "-Wno-unknown-warning-option"]
+# Per-file device flags. The forward: NaNs are not data there (inputs are
+# finite; masked scores are -inf), and with the IEEE mode bit off v_max_f32
+# needs no canonicalising copy of each MFMA result before the row-maximum tree
+# (16 instructions per 64-key tile). The backward has no maxima and keeps the
+# defaults (its dK/dV kernel is register-allocated to three workgroups per CU).
+FILE_FLAGS = {"thd_fwd.hip": ["-fno-honor-nans", "-mno-amdgpu-ieee"]}
 
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + COMMON + (DEVICE if src.endswith(".hip") else ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"])
+    cmd = [HIPCC] + COMMON + (DEVICE + FILE_FLAGS.get(src, []) if src.endswith(".hip")
+                              else ["-x", "c++", "-D__HIP_PLATFORM_AMD__", "-I/opt/rocm/include"])
     cmd += ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
@@ -67,7 +70,8 @@ def resources() -> str:
             continue
         asm = os.path.join(BUILD, os.path.splitext(src)[0] + ".s")
         os.makedirs(BUILD, exist_ok=True)
-        cmd = [HIPCC] + COMMON + DEVICE + ["--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm]
+        cmd = [HIPCC] + COMMON + DEVICE + FILE_FLAGS.get(src, []) + [
+            "--cuda-device-only", "-S", os.path.join(CSRC, src), "-o", asm]
         res = subprocess.run(cmd, capture_output=True, text=True)
         if res.returncode != 0:
             raise RuntimeError(res.stderr)

@@ -25,7 +25,10 @@
 //      K^T operand read by ds_read_b64_tr_b16;
 //   dS (and P in dV = P^T dO) enter their products as a pair of bf16 values
 //   (hi, lo = x - hi), so their rounding error is ~2^-17 instead of bf16's
-//   2^-9: the gradients are then limited by fp32 accumulation only;
+//   2^-9: the gradients are then limited by fp32 accumulation only. (With dS
+//   in plain bf16 the backward ran 12% faster, but dK, which sums over the G
+//   heads of a kv head, reached max-abs 0.027 against fp64 at G = 64 and 128,
+//   beyond the 2e-2 bound);
 //   thd_bwd_dkdv_kernel: one workgroup (4 waves, 16 keys each) per
 //      (64-key tile, kv head). The key tiles cover every key once; the query
 //      tiles that see a key tile are a suffix of its document's tiles, walked
@@ -474,8 +477,11 @@ struct RowBlock {
   size_t base;  // index into [T_local * Hq] of the tile's first row
 };
 
+// Three workgroups per CU for d_qk <= 128 (at most 168 registers per lane,
+// which the kernel fits without spilling): one wave's vector work then
+// overlaps two others' MFMAs. The d_qk = 192 kernel needs more and runs two.
 template <int DQK, int DV>
-__global__ __launch_bounds__(kDkvWaves * 64, 2) void thd_bwd_dkdv_kernel(BwdParams p) {
+__global__ __launch_bounds__(kDkvWaves * 64, DQK > 128 ? 2 : 3) void thd_bwd_dkdv_kernel(BwdParams p) {
   using S = DkvShape<DQK, DV>;
   // Separate arrays, so the compiler can tell that reading one stage needs
   // no wait on copies still landing in another.
