@@ -5,8 +5,9 @@
 //
 // 16 threads build, inspect, copy and release metadata for a small set of
 // length lists (so most builds are cache hits and entries are shared), while
-// some threads clear the cache. Every copy must equal the reference copy made
-// before the threads start. Exit status 0 on success.
+// some threads clear the cache. The cases cover plain plans, packed plans
+// (also from real lengths, padded), and pass plans. Every copy must equal the
+// reference copy made before the threads start. Exit status 0 on success.
 #include <atomic>
 #include <cstdio>
 #include <cstdlib>
@@ -17,10 +18,32 @@
 
 namespace {
 
+enum Kind { kPlain, kPacked, kPackedPadded, kPass };
+
 struct Case {
   std::vector<int32_t> lengths;
   int32_t cp, rank, block_t, block_n, concurrency;
+  Kind kind = kPlain;
+  uint64_t shards = 0;   // pass plans
 };
+
+int build(const Case& c, thd_meta** m) {
+  const int32_t n = int32_t(c.lengths.size());
+  switch (c.kind) {
+    case kPacked:
+      return thd_build_packed_metadata(c.lengths.data(), n, c.cp, c.rank, c.block_t, c.block_n,
+                                       c.concurrency, 0, -1, m);
+    case kPackedPadded:
+      return thd_build_packed_metadata(c.lengths.data(), n, c.cp, c.rank, c.block_t, c.block_n,
+                                       c.concurrency, 1, -1, m);
+    case kPass:
+      return thd_build_pass_metadata(c.lengths.data(), n, c.cp, c.rank, c.block_t, c.block_n,
+                                     c.shards, -1, m);
+    default:
+      return thd_build_metadata(c.lengths.data(), n, c.cp, c.rank, c.block_t, c.block_n,
+                                c.concurrency, -1, m);
+  }
+}
 
 std::vector<int32_t> field(const thd_meta* m, int32_t f, int64_t n) {
   std::vector<int32_t> out(size_t(n > 0 ? n : 0));
@@ -32,7 +55,8 @@ std::vector<int32_t> field(const thd_meta* m, int32_t f, int64_t n) {
 }
 
 struct Snapshot {
-  std::vector<int32_t> q_global, kv_row, tiles, kvtiles, items, splits;
+  std::vector<int32_t> q_global, kv_row, tiles, kvtiles, items, splits, pack_rows, pack_keys,
+      doc_end;
 };
 
 Snapshot take(const thd_meta* m) {
@@ -46,14 +70,18 @@ Snapshot take(const thd_meta* m) {
   s.kv_row = field(m, THD_FIELD_KV_ROW, info.total_tokens);
   s.tiles = field(m, THD_FIELD_TILES, info.n_tiles * 8);
   s.kvtiles = field(m, THD_FIELD_KVTILES, info.n_kvtiles * 8);
-  s.items = field(m, THD_FIELD_ITEMS, info.n_items * 4);
-  s.splits = field(m, THD_FIELD_SPLITS, info.n_splits * 4);
+  s.items = field(m, THD_FIELD_ITEMS, info.n_items * info.item_ints);
+  s.splits = field(m, THD_FIELD_SPLITS, (info.is_pass ? info.n_tiles : info.n_splits) * 4);
+  s.pack_rows = field(m, THD_FIELD_PACK_ROWS, info.n_pack_rows * 4);
+  s.pack_keys = field(m, THD_FIELD_PACK_KEYS, info.n_pack_keys);
+  s.doc_end = field(m, THD_FIELD_DOC_END, info.n_docs);
   return s;
 }
 
 bool same(const Snapshot& a, const Snapshot& b) {
   return a.q_global == b.q_global && a.kv_row == b.kv_row && a.tiles == b.tiles &&
-         a.kvtiles == b.kvtiles && a.items == b.items && a.splits == b.splits;
+         a.kvtiles == b.kvtiles && a.items == b.items && a.splits == b.splits &&
+         a.pack_rows == b.pack_rows && a.pack_keys == b.pack_keys && a.doc_end == b.doc_end;
 }
 
 }  // namespace
@@ -66,12 +94,16 @@ int main() {
       {{1000, 72, 600}, 4, 3, 32, 64, 0},
       {{4096, 96}, 4, 0, 16, 64, 8},
       {{16, 32, 1040, 16, 400}, 8, 3, 8, 64, 0},
+      {{16, 48, 8, 80, 16, 8, 32}, 2, 1, 8, 32, 0, kPacked},
+      {{16 * 1, 16 * 2, 16 * 3, 16 * 5, 16 * 8, 16 * 13, 16 * 21}, 8, 0, 16, 32, 84, kPacked},
+      {{5, 13, 8, 3, 30, 1, 22}, 2, 0, 32, 64, 0, kPackedPadded},
+      {{16, 32, 1040, 16, 400}, 8, 3, 32, 64, 0, kPass, 0x9u},
+      {{256, 512, 256}, 2, 1, 64, 64, 0, kPass, 0x2u},
   };
   std::vector<Snapshot> ref;
   for (const Case& c : cases) {
     thd_meta* m = nullptr;
-    if (thd_build_metadata(c.lengths.data(), int32_t(c.lengths.size()), c.cp, c.rank, c.block_t,
-                           c.block_n, c.concurrency, -1, &m) != THD_OK) {
+    if (build(c, &m) != THD_OK) {
       std::fprintf(stderr, "build failed: %s\n", thd_last_error());
       return 2;
     }
@@ -86,8 +118,7 @@ int main() {
         const size_t k = size_t(t * 7 + it) % cases.size();
         const Case& c = cases[k];
         thd_meta* m = nullptr;
-        if (thd_build_metadata(c.lengths.data(), int32_t(c.lengths.size()), c.cp, c.rank,
-                               c.block_t, c.block_n, c.concurrency, -1, &m) != THD_OK) {
+        if (build(c, &m) != THD_OK) {
           ++bad;
           continue;
         }
