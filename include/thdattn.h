@@ -354,13 +354,13 @@ int thd_build_pass_metadata(const int32_t* seqlens, int32_t n_docs, int32_t cp, 
                             int32_t block_t, int32_t block_n, uint64_t shard_mask,
                             int32_t device, thd_meta** out);
 
-/* Bytes a pass needs: parts_bytes of workspace (partial results of its work
- * items; may be NULL) and state_bytes of running state (fp32 O
- * [T_local, Hq, d_v] then its base-2 log-sum-exp [T_local, Hq]; may be NULL).
- * The state is the caller's and lives across the passes of one forward.
- * Errors: THD_EINVAL, THD_EMISMATCH (not a pass plan). */
-int thd_attn_fwd_pass_workspace(const thd_meta* meta, int32_t hq, int32_t hkv, int32_t d_v,
-                                int64_t* parts_bytes, int64_t* state_bytes);
+/* Bytes of running state the passes of one forward share (the caller's;
+ * fp32 O [T_local, Hq, d_v] then its base-2 log-sum-exp [T_local, Hq]). A
+ * pass needs no other workspace. Source: as thd_build_pass_metadata.
+ * Errors: THD_EINVAL (bad heads, d_v < 1, NULL state_bytes), THD_EMISMATCH
+ * (not a pass plan). */
+int thd_attn_fwd_pass_state_bytes(const thd_meta* meta, int32_t hq, int32_t hkv, int32_t d_v,
+                                  int64_t* state_bytes);
 
 #define THD_PASS_FIRST 1   /* the state holds nothing yet (its contents are ignored) */
 #define THD_PASS_LAST 2    /* write o and lse instead of the state */
@@ -369,16 +369,19 @@ int thd_attn_fwd_pass_workspace(const thd_meta* meta, int32_t hq, int32_t hkv, i
  * merged (log-sum-exp weights) into the state; with THD_PASS_LAST the merged
  * result is written to o (bf16) and lse (natural log) instead. Rows that saw
  * no key in any pass so far hold an empty state (lse -inf; written as O = 0,
- * LSE = -inf by a last pass). Arguments and layouts as thd_attn_fwd (o and lse
- * may be NULL unless THD_PASS_LAST); state (16-byte aligned, state_bytes of
- * thd_attn_fwd_pass_workspace); workspace (16-byte aligned, parts_bytes).
- * Every key a pass reads lies in its shards' rows of k and v, so the other
- * rows may still be in flight. Errors as thd_attn_fwd, plus THD_EMISMATCH
- * (metadata not a pass plan) and THD_EINVAL (unknown flags). */
+ * LSE = -inf by a last pass). One workgroup per query tile and kv head walks
+ * all of the tile's runs in the pass and merges straight into the state, so a
+ * pass allocates nothing and launches one kernel. Arguments and layouts as
+ * thd_attn_fwd (o and lse may be NULL unless THD_PASS_LAST); state (16-byte
+ * aligned, thd_attn_fwd_pass_state_bytes long). Every key a pass reads lies in
+ * its shards' rows of k and v, so the other rows may still be in flight.
+ * Passes of one forward run in order on one stream (each reads the state the
+ * last one wrote). Errors as thd_attn_fwd, plus THD_EMISMATCH (metadata not a
+ * pass plan) and THD_EINVAL (unknown flags). */
 int thd_attn_fwd_pass(const thd_meta* meta, const void* q, const void* k, const void* v,
                       void* o, float* lse, float* state, int32_t flags, int32_t hq,
                       int32_t hkv, int32_t d_qk, int32_t d_v, float softmax_scale,
-                      void* workspace, int64_t workspace_bytes, void* hip_stream);
+                      void* hip_stream);
 
 /* Bytes of device workspace thd_attn_bwd needs (caller allocates): D and
  * the base-2 log-sum-exp, two fp32 [T_local, Hq] arrays. Errors: THD_EINVAL. */

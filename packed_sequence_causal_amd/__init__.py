@@ -92,9 +92,9 @@ def _load():
                                                 ctypes.c_float, p]),
         "thd_build_pass_metadata": (ctypes.c_int, [pi32, i32, i32, i32, i32, i32, ctypes.c_uint64,
                                                    i32, ctypes.POINTER(p)]),
-        "thd_attn_fwd_pass_workspace": (ctypes.c_int, [p, i32, i32, i32, pi64, pi64]),
+        "thd_attn_fwd_pass_state_bytes": (ctypes.c_int, [p, i32, i32, i32, pi64]),
         "thd_attn_fwd_pass": (ctypes.c_int, [p, p, p, p, p, p, p, i32, i32, i32, i32, i32,
-                                             ctypes.c_float, p, i64, p]),
+                                             ctypes.c_float, p]),
         "thd_attn_bwd_workspace": (ctypes.c_int, [p, i32, pi64]),
         "thd_attn_bwd": (ctypes.c_int, [p, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
                                         ctypes.c_float, p, i64, p]),
@@ -112,7 +112,7 @@ EXPORTS = ("thd_last_error", "thd_plan_partition", "thd_build_metadata", "thd_pa
            "thd_meta_copy", "thd_meta_release", "thd_cache_stats", "thd_cache_clear",
            "thd_preferred_tiles", "thd_preferred_fwd_tiles", "thd_fwd_concurrency",
            "thd_attn_fwd_workspace", "thd_attn_fwd", "thd_attn_fwd_noalloc",
-           "thd_build_pass_metadata", "thd_attn_fwd_pass_workspace", "thd_attn_fwd_pass",
+           "thd_build_pass_metadata", "thd_attn_fwd_pass_state_bytes", "thd_attn_fwd_pass",
            "thd_attn_bwd_workspace", "thd_attn_bwd")
 PASS_FIRST = 1
 PASS_LAST = 2
@@ -438,10 +438,10 @@ def build_pass_metadata(*, seqlens, cp: int, rank: int, block_t: int, block_n: i
 
 
 def pass_state(*, meta: Meta, hq: int, hkv: int, d_v: int, device):
-    """A state buffer (fp32) for the passes of one forward (thd_attn_fwd_pass_workspace)."""
+    """A state buffer (fp32) for the passes of one forward (thd_attn_fwd_pass_state_bytes)."""
     torch = _torch()
     state = ctypes.c_int64()
-    _check(_lib.thd_attn_fwd_pass_workspace(meta.handle, hq, hkv, d_v, None, ctypes.byref(state)))
+    _check(_lib.thd_attn_fwd_pass_state_bytes(meta.handle, hq, hkv, d_v, ctypes.byref(state)))
     return torch.empty(state.value // 4, dtype=torch.float32, device=device)
 
 
@@ -471,17 +471,12 @@ def attn_fwd_pass(*, q, k, v, meta: Meta, state, first: bool, last: bool, out=No
             lse = torch.empty((t_loc, hq), dtype=torch.float32, device=dev)
         else:
             _need("lse", lse, torch.float32, (t_loc, hq), dev)
-    parts = ctypes.c_int64()
-    _check(_lib.thd_attn_fwd_pass_workspace(meta.handle, hq, hkv, d_v, ctypes.byref(parts), None))
-    ws = _scratch(dev, parts.value, stream)
     flags = (PASS_FIRST if first else 0) | (PASS_LAST if last else 0)
     scale = 0.0 if softmax_scale is None else float(softmax_scale)
     _check(_lib.thd_attn_fwd_pass(meta.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
                                   None if out is None else out.data_ptr(),
                                   None if lse is None else lse.data_ptr(), state.data_ptr(), flags,
-                                  hq, hkv, d_qk, d_v, scale,
-                                  None if ws is None else ws.data_ptr(), parts.value,
-                                  _stream_handle(stream, dev)))
+                                  hq, hkv, d_qk, d_v, scale, _stream_handle(stream, dev)))
     return (out, lse) if last else None
 
 

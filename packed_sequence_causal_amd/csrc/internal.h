@@ -29,9 +29,14 @@ struct Plan {
   int64_t pad_tokens = 0;
   // A pass plan (all-gather overlap) covers only the keys of the source ranks
   // in shard_mask: its items are 8 ints with absolute key ranges, and splits
-  // holds one [tile, first part slot, parts, 0] record per tile.
+  // holds one [tile, first part slot, parts, 0] record per tile. For the
+  // kernel: pass_runs lists the items by part slot (so a tile's runs are
+  // consecutive), pass_order the tiles with runs, most KV tiles first, then
+  // the tiles without (n_run_tiles of the former).
   bool pass = false;
   uint64_t shard_mask = 0;
+  std::vector<int32_t> pass_runs, pass_order;
+  int64_t n_run_tiles = 0;
   // A packed plan (short-segment packing) also lists packed tiles
   // (q_local_start = -1): their rows in pack_rows [local row, first slot, last
   // slot, real] and their key slots' gathered rows in pack_keys. It has no
@@ -80,6 +85,8 @@ struct DeviceMeta {
   const int32_t* doc_end = nullptr;
   const int32_t* pack_rows = nullptr;
   const int32_t* pack_keys = nullptr;
+  const int32_t* pass_runs = nullptr;
+  const int32_t* pass_order = nullptr;
 };
 
 struct MetaEntry {
@@ -115,6 +122,7 @@ struct FwdParams {
   float* lse;
   float* o_f32;       // optional fp32 copy of O (split P in the PV product); null to skip
   float* partial;     // workspace: per (part slot, kv head) O rows (fp32) then their lse
+                      // (split tiles of a one-pass plan)
   const int32_t* tiles;
   const int32_t* items;
   const int32_t* splits;
@@ -123,12 +131,15 @@ struct FwdParams {
   int32_t n_items, n_splits, hq, hkv, group, block_t, block_n;
   int64_t total;
   float scale_log2;   // softmax_scale * log2(e)
-  // Pass plans only: items carry absolute key ranges; the running state
-  // (O [T_local, Hq, d_v] fp32 then its log2-sum-exp [T_local, Hq]) and the
-  // THD_PASS_FIRST / THD_PASS_LAST flags; n_splits counts every tile.
+  // Pass plans only: the running state (O [T_local, Hq, d_v] fp32 then its
+  // log2-sum-exp [T_local, Hq]), the THD_PASS_FIRST / THD_PASS_LAST flags,
+  // each tile's runs (pass_runs, 8 ints each, from splits' first slot) and
+  // the tiles to run (pass_order; n_items of them).
   int32_t ranged, pass_flags;
   float* state;
   int64_t local;
+  const int32_t* pass_runs;
+  const int32_t* pass_order;
   // Packed plans only: rows [local row, first slot, last slot, real] of the
   // packed tiles, and each key slot's gathered row.
   int32_t packed;
@@ -159,7 +170,8 @@ int fwd_static_scratch(int device, void** ptr);
 
 // Kernel launchers (defined in the .hip files). Return a hipError_t value.
 int launch_fwd(const FwdParams& p, int d_qk, int d_v, void* stream);
-// One forward pass of a pass plan (its items, then the merge into the state).
+// One forward pass of a pass plan: each listed tile walks its runs and merges
+// its result into the running state.
 int launch_fwd_pass(const FwdParams& p, int d_qk, int d_v, void* stream);
 // Workgroups of the forward kernel for this KV tile size that fit one CU.
 int fwd_workgroups_per_cu(int block_n);

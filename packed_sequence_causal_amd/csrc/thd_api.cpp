@@ -64,10 +64,11 @@ struct DeviceScope {
 void upload(MetaEntry& e, int device) {
   const Plan& p = *e.plan;
   DeviceScope scope(device);
-  constexpr int kParts = 10;
-  const std::vector<int32_t>* parts[kParts] = {&p.kv_row,  &p.tiles,  &p.order,   &p.kvtiles,
-                                               &p.q_global, &p.items, &p.splits,  &p.doc_end,
-                                               &p.pack_rows, &p.pack_keys};
+  constexpr int kParts = 12;
+  const std::vector<int32_t>* parts[kParts] = {&p.kv_row,    &p.tiles,     &p.order,
+                                               &p.kvtiles,   &p.q_global,  &p.items,
+                                               &p.splits,    &p.doc_end,   &p.pack_rows,
+                                               &p.pack_keys, &p.pass_runs, &p.pass_order};
   size_t offs[kParts];
   size_t bytes = 0;
   for (int i = 0; i < kParts; ++i) {
@@ -98,6 +99,8 @@ void upload(MetaEntry& e, int device) {
   e.dev.doc_end = reinterpret_cast<const int32_t*>(b + offs[7]);
   e.dev.pack_rows = reinterpret_cast<const int32_t*>(b + offs[8]);
   e.dev.pack_keys = reinterpret_cast<const int32_t*>(b + offs[9]);
+  e.dev.pass_runs = reinterpret_cast<const int32_t*>(b + offs[10]);
+  e.dev.pass_order = reinterpret_cast<const int32_t*>(b + offs[11]);
 }
 
 // Least-recently-used cache of metadata entries. Entries still referenced by a
@@ -625,24 +628,21 @@ int thd_build_pass_metadata(const int32_t* seqlens, int32_t n_docs, int32_t cp, 
   });
 }
 
-int thd_attn_fwd_pass_workspace(const thd_meta* meta, int32_t hq, int32_t hkv, int32_t d_v,
-                                int64_t* parts_bytes, int64_t* state_bytes) {
+int thd_attn_fwd_pass_state_bytes(const thd_meta* meta, int32_t hq, int32_t hkv, int32_t d_v,
+                                  int64_t* state_bytes) {
   return guarded([&] {
     const Plan& p = *entry_of(meta).plan;
     check_heads(hq, hkv);
     if (d_v < 1) fail(THD_EINVAL, "d_v must be >= 1");
     if (!p.pass) fail(THD_EMISMATCH, "metadata is not a pass plan");
-    if (parts_bytes != nullptr)
-      *parts_bytes = p.n_part_slots * hkv * fwd_partial_floats(p.block_t, hq / hkv, d_v) *
-                     int64_t(sizeof(float));
-    if (state_bytes != nullptr) *state_bytes = p.local * hq * (int64_t(d_v) + 1) * int64_t(sizeof(float));
+    if (state_bytes == nullptr) fail(THD_EINVAL, "state_bytes is NULL");
+    *state_bytes = p.local * hq * (int64_t(d_v) + 1) * int64_t(sizeof(float));
   });
 }
 
 int thd_attn_fwd_pass(const thd_meta* meta, const void* q, const void* k, const void* v, void* o,
                       float* lse, float* state, int32_t flags, int32_t hq, int32_t hkv,
-                      int32_t d_qk, int32_t d_v, float softmax_scale, void* workspace,
-                      int64_t workspace_bytes, void* hip_stream) {
+                      int32_t d_qk, int32_t d_v, float softmax_scale, void* hip_stream) {
   return guarded([&] {
     const MetaEntry& e = entry_of(meta);
     const Plan& p = *e.plan;
@@ -665,19 +665,12 @@ int thd_attn_fwd_pass(const thd_meta* meta, const void* q, const void* k, const 
       check_ptr(o, "o", 16);
       check_ptr(lse, "lse", 16);
     }
-    const int64_t need = p.n_part_slots * hkv * fwd_partial_floats(p.block_t, group, d_v) *
-                         int64_t(sizeof(float));
-    if (need > 0) {
-      check_ptr(workspace, "workspace", 16);
-      if (workspace_bytes < need)
-        fail(THD_EINVAL, "workspace has " + std::to_string(workspace_bytes) + " bytes, needs " +
-                             std::to_string(need));
-    }
     const DeviceMeta& d = device_meta(e);
-    const int64_t n_items = int64_t(p.items.size() / 8);
     const int64_t n_tiles = int64_t(p.tiles.size() / 8);
-    if (n_items * hkv >= (int64_t(1) << 31) || n_tiles * hkv >= (int64_t(1) << 31))
-      fail(THD_ERANGE, "grid too large");
+    if (n_tiles * hkv >= (int64_t(1) << 31)) fail(THD_ERANGE, "grid too large");
+    // A first pass sets every row's state and a last one writes every row's
+    // output, so they visit every tile; the others only the tiles with runs.
+    const int64_t n_wg = (flags & (THD_PASS_FIRST | THD_PASS_LAST)) != 0 ? n_tiles : p.n_run_tiles;
     check_kv_bytes(p.total, hkv, d_qk, d_v);
     FwdParams fp{};
     fp.q = q;
@@ -686,14 +679,16 @@ int thd_attn_fwd_pass(const thd_meta* meta, const void* q, const void* k, const 
     fp.o = o;
     fp.lse = lse;
     fp.o_f32 = nullptr;
-    fp.partial = static_cast<float*>(workspace);
+    fp.partial = nullptr;
     fp.tiles = d.tiles;
     fp.items = d.items;
     fp.splits = d.splits;
     fp.kv_row = d.kv_row;
     fp.doc_end = d.doc_end;
-    fp.n_items = int32_t(n_items);
+    fp.n_items = int32_t(n_wg);
     fp.n_splits = int32_t(n_tiles);
+    fp.pass_runs = d.pass_runs;
+    fp.pass_order = d.pass_order;
     fp.hq = hq;
     fp.hkv = hkv;
     fp.group = group;

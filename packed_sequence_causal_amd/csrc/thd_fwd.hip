@@ -141,8 +141,10 @@ struct FwdShape {
 template <int BN>
 constexpr int kFwdOccupancy = BN == kBlockNShort ? 3 : 2;
 
-// RANGED: items of a pass plan (all-gather overlap), 8 ints with an absolute
-// key range [first key, end key) per item, always written as a part.
+// RANGED: one forward pass of a pass plan (all-gather overlap): a workgroup
+// takes one tile (p.pass_order) and walks each of the tile's runs (absolute
+// key ranges [first key, end key), p.pass_runs) in turn with the same online
+// softmax, then merges its result straight into the caller's running state.
 // PACKED: a packed plan's items, some of whose tiles are packed tiles (rows of
 // several documents; short-segment packing): such a tile's rows, their key
 // windows and its key slots come from pack_rows / pack_keys, every KV tile
@@ -168,13 +170,28 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
   int lrow = lane & 31;
 
   // Work item: KV tiles [kv_begin, kv_end) of one query tile (a whole tile
-  // unless its key range is split), for kv head blockIdx.x % Hkv.
+  // unless its key range is split), for kv head blockIdx.x % Hkv. A pass
+  // (RANGED) takes a whole tile and its n_runs runs of this pass's keys.
   const int kvh = blockIdx.x % p.hkv;
-  const int32_t* item = p.items + size_t(blockIdx.x / p.hkv) * (RANGED ? 8 : 4);
-  const int tile = item[0];
-  const int kv_begin = RANGED ? 0 : item[1];
-  const int kv_end = RANGED ? item[4] : item[2];
-  const int part = item[3];
+  int tile, kv_begin, kv_end, part, n_runs = 1;
+  const int32_t* item;
+  const int32_t* runs = nullptr;
+  if constexpr (RANGED) {
+    const int32_t* sp = p.splits + size_t(p.pass_order[blockIdx.x / p.hkv]) * 4;
+    tile = sp[0];
+    n_runs = sp[2];
+    runs = p.pass_runs + size_t(sp[1]) * 8;
+    item = runs;
+    kv_begin = 0;
+    kv_end = n_runs > 0 ? runs[4] : 0;
+    part = -1;
+  } else {
+    item = p.items + size_t(blockIdx.x / p.hkv) * 4;
+    tile = item[0];
+    kv_begin = item[1];
+    kv_end = item[2];
+    part = item[3];
+  }
   const int32_t* td = p.tiles + size_t(tile) * 8;
   // A packed tile's td[1] is its first row in pack_rows and td[5] its first
   // key slot; its slots are numbered from 0 and fill td[6] whole KV tiles.
@@ -184,14 +201,14 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
   const int n_rows = td[2];
   // KV tiles start at the document's first key (a pass plan's item: at its
   // run's first key); keys from key_hi on are seen by no row of the item.
-  const int kv_start = RANGED ? item[1] : (packed_tile ? 0 : td[5]);
-  const int n_full = RANGED ? item[5] : td[7];
-  const int key_hi = RANGED ? item[2] : (packed_tile ? td[6] * BN : q_glob0 + n_rows);
+  int kv_start = RANGED ? (n_runs > 0 ? item[1] : 0) : (packed_tile ? 0 : td[5]);
+  int n_full = RANGED ? (n_runs > 0 ? item[5] : 0) : td[7];
+  int key_hi = RANGED ? (n_runs > 0 ? item[2] : 1) : (packed_tile ? td[6] * BN : q_glob0 + n_rows);
   // Rows at or past the document's last real token are padding: written as
   // O = 0, LSE = +inf (tokens are in position order within a plain tile; a
   // packed row carries its own flag).
   const int n_real = packed_tile ? 0 : min(max(p.doc_end[td[3]] - q_glob0, 0), n_rows);
-  const int key_last = key_hi - 1;
+  int key_last = key_hi - 1;
 
   // Row block rb of this wave holds rows 32 * (RB * wave + rb) + lane % 32.
   const int G = p.group;
@@ -332,6 +349,8 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
   }
   const float c2 = p.scale_log2;
 
+  // The keys of one item (of one run, for a pass): prologue, then the loop.
+  auto walk = [&]() __attribute__((always_inline)) {
   // Prologue: rows of the first two KV tiles, then the first tile's data.
   fetch_rows(kv_begin, rows_cur);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
@@ -573,6 +592,28 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
     step(j, smem0, smem1);
     if (j + 1 < kv_end) step(j + 1, smem1, smem0);
   }
+  };
+  if constexpr (RANGED) {
+    // A pass walks each run of the tile; the causal limit of every row is
+    // also clamped to the run's end. The loop drains its copies and ends on
+    // a barrier, so the next run's prologue may refill the ring.
+    for (int r = 0; r < n_runs; ++r) {
+      if (r > 0) {
+        const int32_t* ru = runs + size_t(r) * 8;
+        kv_start = ru[1];
+        key_hi = ru[2];
+        kv_end = ru[4];
+        n_full = ru[5];
+        key_last = key_hi - 1;
+      }
+#pragma unroll
+      for (int rb = 0; rb < RB; ++rb)
+        qpos[rb] = valid[rb] ? min(q_glob0 + tok[rb], key_last) : INT_MAX;
+      walk();
+    }
+  } else {
+    walk();
+  }
 
   static_assert(RB == 1, "the epilogue stages one 32-row block per wave");
   if (!wave_active) return;
@@ -592,6 +633,64 @@ __global__ __launch_bounds__(kFwdThreads, kFwdOccupancy<BN_>) void thd_fwd_kerne
   }
   const float l_tot = l_run[0] + __shfl_xor(l_run[0], 32);
   const float inv = 1.0f / l_tot;
+  if constexpr (RANGED) {
+    // Merge into the running state: per row, this pass's (O, log2-sum-exp)
+    // and the state's, weighted by 2^(lse2 - max) (THD_PASS_FIRST: the state
+    // counts as empty). THD_PASS_LAST writes O (bf16; pad rows 0) and LSE
+    // (natural log; pad rows +inf), otherwise the merged state. Each row of a
+    // tile belongs to this one workgroup in a pass; the row's two lanes read
+    // its lse2 in the same instruction before one of them stores the new one.
+    if (!valid[0]) return;
+    const bool first = (p.pass_flags & THD_PASS_FIRST) != 0;
+    const bool last = (p.pass_flags & THD_PASS_LAST) != 0;
+    const size_t orow = size_t(q_local0 + tok[0]) * p.hq + head[0];
+    float* st_o = p.state + orow * DV;
+    float* st_l = p.state + size_t(p.local) * p.hq * DV + orow;
+    const bool own_any = l_tot > 0.0f;   // no run, or (never) no visible key
+    const float own = own_any ? m_run[0] + __builtin_amdgcn_logf(l_tot) : -INFINITY;
+    const float ls = first ? -INFINITY : *st_l;
+    const float mx = fmaxf(own, ls);
+    float w_own = 0.0f, w_st = 0.0f, lnew = -INFINITY, norm = 0.0f;
+    if (mx > -INFINITY) {
+      w_own = own_any ? __builtin_amdgcn_exp2f(own - mx) : 0.0f;
+      w_st = ls > -INFINITY ? __builtin_amdgcn_exp2f(ls - mx) : 0.0f;
+      lnew = mx + __builtin_amdgcn_logf(w_own + w_st);
+      norm = 1.0f / (w_own + w_st);
+    }
+    const float a_own = own_any ? w_own * inv * norm : 0.0f;   // weight of acc
+    const float a_st = w_st * norm;
+    const bool pad = last && q_glob0 + tok[0] >= p.doc_end[td[3]];
+#pragma unroll
+    for (int b = 0; b < S::DVB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int col = 32 * b + 8 * g + 4 * half;
+        f32x4 o4;
+        if (a_st != 0.0f) {
+          const f32x4 s4 = *reinterpret_cast<const f32x4*>(st_o + col);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = __builtin_fmaf(acc[0][b][4 * g + e], a_own, s4[e] * a_st);
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o4[e] = acc[0][b][4 * g + e] * a_own;
+        }
+        if (last) {
+          bf16x4 out;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) out[e] = static_cast<__bf16>(pad ? 0.0f : o4[e]);
+          *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.o) + orow * DV + col) = out;
+        } else {
+          *reinterpret_cast<f32x4*>(st_o + col) = o4;
+        }
+      }
+    if (half == 0) {
+      if (last)
+        p.lse[orow] = pad ? INFINITY : lnew * kLn2;
+      else
+        *st_l = lnew;
+    }
+    return;
+  }
   if (part >= 0) {
     // Part of a split tile: its O normalised by its own sum, and its
     // log2-sum-exp, for the combine kernel.
@@ -709,98 +808,13 @@ __global__ __launch_bounds__(256) void thd_fwd_combine_kernel(FwdParams p) {
   if (col == 0) p.lse[orow] = pad ? INFINITY : (mx + __builtin_amdgcn_logf(wsum)) * kLn2;
 }
 
-// Merges a pass's parts into the running state: per row, the state's
-// (O, lse2) and each part's, weighted by 2^(lse2 - max) (THD_PASS_FIRST: the
-// state counts as empty). THD_PASS_LAST writes O (bf16; pad rows 0) and LSE
-// (natural log; pad rows +inf); otherwise the merged state. One thread per
-// (tile, kv head, row, 4 columns). The threads of one row lie in one wave (a
-// row's DV / 4 threads are consecutive and divide 64): the state's lse2 of the
-// row is loaded by all of them in one instruction before the row's first
-// thread stores the new one, which depends on that load.
-template <int DV>
-__global__ __launch_bounds__(256) void thd_fwd_pass_combine_kernel(FwdParams p) {
-  constexpr int CPR = DV / 4;
-  static_assert(64 % CPR == 0, "a row's threads must lie in one wave");
-  const int G = p.group;
-  const int rows = p.block_t * G;
-  const int64_t idx = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  const int64_t per_tile = int64_t(p.hkv) * rows * CPR;
-  if (idx >= per_tile * p.n_splits) return;
-  const int t = int(idx / per_tile);
-  int rem = int(idx - t * per_tile);
-  const int kvh = rem / (rows * CPR);
-  rem -= kvh * rows * CPR;
-  const int row = rem / CPR;
-  const int col = (rem - row * CPR) * 4;
-  const int32_t* sp = p.splits + size_t(t) * 4;
-  const int tile = sp[0], first = sp[1], n_parts = sp[2];
-  const bool first_pass = (p.pass_flags & THD_PASS_FIRST) != 0;
-  const bool last = (p.pass_flags & THD_PASS_LAST) != 0;
-  if (n_parts == 0 && !last && !first_pass) return;   // the state stays as it is
-  const int32_t* td = p.tiles + size_t(tile) * 8;
-  const int tok = row / G;
-  if (tok >= td[2]) return;
-  const int head = kvh * G + (row - tok * G);
-  const size_t orow = size_t(td[0] + tok) * p.hq + head;
-  float* st_o = p.state + orow * DV + col;
-  float* st_l = p.state + size_t(p.local) * p.hq * DV + orow;
-  const float ls = first_pass ? -INFINITY : *st_l;
-  const size_t slot_floats = size_t(fwd_partial_floats(p.block_t, G, DV));
-  const float* base0 = p.partial + (size_t(first) * p.hkv + kvh) * slot_floats;
-  const size_t part_stride = size_t(p.hkv) * slot_floats;
-  float mx = ls;
-  for (int q = 0; q < n_parts; ++q) mx = fmaxf(mx, base0[q * part_stride + size_t(rows) * DV + row]);
-  f32x4 o4 = {};
-  float lnew = -INFINITY;
-  if (mx > -INFINITY) {
-    float wsum = 0.0f;
-    f32x4 acc = {};
-    if (ls > -INFINITY) {
-      const float w = __builtin_amdgcn_exp2f(ls - mx);
-      wsum += w;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(st_o);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = w * v[e];
-    }
-    for (int q = 0; q < n_parts; ++q) {
-      const float* base = base0 + q * part_stride;
-      const float w = __builtin_amdgcn_exp2f(base[size_t(rows) * DV + row] - mx);
-      wsum += w;
-      const f32x4 v = *reinterpret_cast<const f32x4*>(base + size_t(row) * DV + col);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) acc[e] = __builtin_fmaf(w, v[e], acc[e]);
-    }
-    const float inv = 1.0f / wsum;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) o4[e] = acc[e] * inv;
-    lnew = mx + __builtin_amdgcn_logf(wsum);
-  }
-  if (last) {
-    const bool pad = td[1] + tok >= p.doc_end[td[3]];
-    bf16x4 out;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) out[e] = static_cast<__bf16>(pad ? 0.0f : o4[e]);
-    *reinterpret_cast<bf16x4*>(static_cast<__bf16*>(p.o) + orow * DV + col) = out;
-    if (col == 0) p.lse[orow] = pad ? INFINITY : lnew * kLn2;
-  } else {
-    *reinterpret_cast<f32x4*>(st_o) = o4;
-    if (col == 0) *st_l = lnew;
-  }
-}
-
 template <int DQK, int DV>
 int launch_pass(const FwdParams& p, void* stream) {
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  if (p.n_items > 0) {
-    hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV, false, kBlockN, true>),
-                       dim3(unsigned(int64_t(p.n_items) * p.hkv)), dim3(kFwdThreads), 0, st, p);
-    const hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return int(err);
-  }
-  const int64_t threads = int64_t(p.n_splits) * p.hkv * p.block_t * p.group * (DV / 4);
-  if (threads == 0) return int(hipSuccess);
-  hipLaunchKernelGGL((thd_fwd_pass_combine_kernel<DV>), dim3(unsigned((threads + 255) / 256)),
-                     dim3(256), 0, st, p);
+  // p.n_items workgroups per kv head: the pass's tiles, in p.pass_order.
+  if (p.n_items == 0) return int(hipSuccess);
+  hipLaunchKernelGGL((thd_fwd_kernel<DQK, DV, false, kBlockN, true>),
+                     dim3(unsigned(int64_t(p.n_items) * p.hkv)), dim3(kFwdThreads), 0,
+                     static_cast<hipStream_t>(stream), p);
   return int(hipGetLastError());
 }
 

@@ -368,6 +368,18 @@ std::unique_ptr<Plan> build_pass_plan(const int32_t* seqlens, int32_t n_docs, in
   });
   p.items.reserve(natural.size());
   for (int32_t i : idx) p.items.insert(p.items.end(), &natural[size_t(i) * 8], &natural[size_t(i) * 8] + 8);
+  // The kernel's view: runs in part-slot order (a tile's runs consecutive),
+  // and the tiles with runs by their KV tiles, most first (stable), then the
+  // tiles without runs (which a first or last pass still visits).
+  p.pass_runs = natural;
+  std::vector<int64_t> work(size_t(n_tiles), 0);
+  for (int64_t i = 0; i < n_items; ++i) work[size_t(natural[size_t(i) * 8])] += natural[size_t(i) * 8 + 4];
+  std::vector<int32_t> with, without;
+  for (int64_t t = 0; t < n_tiles; ++t) (p.splits[size_t(t) * 4 + 2] > 0 ? with : without).push_back(int32_t(t));
+  std::stable_sort(with.begin(), with.end(), [&](int32_t a, int32_t b) { return work[size_t(a)] > work[size_t(b)]; });
+  p.n_run_tiles = int64_t(with.size());
+  p.pass_order = with;
+  p.pass_order.insert(p.pass_order.end(), without.begin(), without.end());
   return plan;
 }
 

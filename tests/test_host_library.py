@@ -445,11 +445,11 @@ def test_pass_metadata_errors():
     assert b"pass" in lib.thd_last_error()
     m = thd.build_metadata(seqlens=[256], cp=1, rank=0, block_t=32, block_n=64)
     assert lib.thd_attn_fwd_pass(m.handle, ptr, ptr, ptr, ptr, ptr, ptr, 3, 32, 8, 128, 128, 0.0,
-                                 None, 0, None) == -5
+                                 None) == -5
     assert lib.thd_attn_fwd_pass(mp.handle, ptr, ptr, ptr, ptr, ptr, ptr, 4, 32, 8, 128, 128, 0.0,
-                                 None, 0, None) == -1
+                                 None) == -1
     n = ctypes.c_int64()
-    assert lib.thd_attn_fwd_pass_workspace(m.handle, 32, 8, 128, ctypes.byref(n), None) == -5
+    assert lib.thd_attn_fwd_pass_state_bytes(m.handle, 32, 8, 128, ctypes.byref(n)) == -5
 
 
 def _compare_packed(lengths, cp, rank, bt, bn, concurrency, real=None):
