@@ -36,12 +36,23 @@ def _state_views(state, t_loc, hq, dv):
     return state[:n].view(t_loc, hq, dv), state[n:].view(t_loc, hq)
 
 
+def _order(kind, cp, rank):
+    if kind == "local_first":
+        return [rank] + [s for s in range(cp) if s != rank][::-1]
+    if kind == "ascending":     # the last shard may hold no key of a tile's rows
+        return list(range(cp))
+    return list(range(cp))[::-1]   # descending: so may the first
+
+
+@pytest.mark.parametrize("order_kind", ["local_first", "ascending", "descending"])
 @pytest.mark.parametrize("case", CASES, ids=lambda c: f"seed{c[0]}")
-def test_shards_one_at_a_time_match_oracle(case):
+def test_shards_one_at_a_time_match_oracle(case, order_kind):
     """Shard s is copied into a NaN-filled gathered K/V only after the pass
     before it has run, so a pass reading any row outside its shard would turn
     its rows into NaN. After each pass the state is the attention over the
-    shards delivered so far; after the last, o and lse are the forward's."""
+    shards delivered so far; after the last, o and lse are the forward's. The
+    orders make first and last passes in which some tiles have no run (their
+    rows' state must still be set, and read out)."""
     seed, lengths, cp, rank, hq, hkv, dqk, dv = case
     b = workloads.small_case(seed, lengths, cp, hq, hkv, dqk, dv, rank=rank)
     dev = device()
@@ -49,7 +60,7 @@ def test_shards_one_at_a_time_match_oracle(case):
     q, k_src, v_src = b.q.to(dev), b.k.to(dev), b.v.to(dev)
     k = torch.full_like(k_src, float("nan"))
     v = torch.full_like(v_src, float("nan"))
-    order = [rank] + [s for s in range(cp) if s != rank][::-1]
+    order = _order(order_kind, cp, rank)
     print(f"[ag] seed={seed} cp={cp} rank={rank} order={order}", flush=True)
     copy = torch.cuda.Stream(device=dev)
     compute = torch.cuda.current_stream(dev)
