@@ -1,15 +1,14 @@
-"""Edge shapes of the HIP path against the fp64 oracle, on an MI355X.
+"""Seeded sweep of random shapes on an MI355X against the fp64 oracle.
 
-The other GPU tests cover the workloads' shapes; this grid covers the rest of
-the supported space: group sizes from 1 to the maximum 128 (a query tile of a
-single token), groups that do not divide 128 or the 32-row backward blocks,
-context-parallel sizes 1 to 16 with first, middle and last ranks, documents of
-the minimum length 2*cp (one row per chunk) beside long ones, and every
-supported head-dimension pair. Each case runs the forward (bf16 P, and split
-probabilities with the fp32 O), the forward with the finest split of long key
-ranges the planner makes, and the backward along both D paths, and compares
-every output element with the oracle.
+Each case draws a context-parallel size and rank, a handful of document
+lengths (from a single token per chunk up to several KV tiles), a head layout
+(MHA, GQA with groups 2 to 8, expanded MLA) and a split concurrency, then
+checks on every element: the forward (the plan's own tiles), the packed-plan
+forward, the backward on both D paths, and a forward run shard by shard.
+The draws come from numpy's generator seeded by the case number, so every
+case is fixed and printed before it runs.
 """
+import numpy as np
 import pytest
 import torch
 
@@ -21,59 +20,70 @@ pytestmark = pytest.mark.gpu
 
 thd = pytest.importorskip("packed_sequence_causal_amd")
 
-GRID = [
-    # (seed, lengths, cp, rank, hq, hkv, dqk, dv)
-    (91, [4, 12, 36], 2, 1, 128, 1, 64, 64),                 # group 128: one token per tile
-    (92, [8, 40, 4], 2, 0, 64, 1, 128, 128),                 # group 64: two 32-row blocks a token
-    (93, [8, 64, 200], 4, 3, 64, 2, 128, 128),               # group 32, last rank
-    (94, [10, 70, 330], 5, 4, 16, 8, 128, 128),              # group 2, cp 5
-    (95, [12, 36, 600], 6, 2, 10, 2, 64, 64),                # group 5: 125-row tiles
-    (96, [14, 140, 546], 7, 5, 14, 2, 192, 128),             # group 7, expanded-MLA dims
-    (97, [6, 6, 6, 6, 6, 600], 3, 0, 24, 4, 128, 128),       # group 6, one-row chunks
-    (98, [2, 2, 1022], 1, 0, 4, 4, 192, 128),                # cp 1, group 1
-    (99, [16] * 10 + [512], 8, 7, 64, 8, 128, 128),          # cp 8, last rank, minimal documents
-    (100, [32, 96, 640], 16, 9, 16, 4, 128, 128),            # cp 16: chunks of 1 to 20 tokens
-]
+HEADS = [(8, 8, 64, 64), (16, 4, 128, 128), (12, 4, 128, 128), (32, 8, 128, 128),
+         (4, 1, 64, 64), (6, 2, 128, 128), (8, 8, 192, 128), (64, 8, 128, 128)]
 
 
-def _ids(c):
-    return f"seed{c[0]}-g{c[4] // c[5]}-cp{c[2]}r{c[3]}-d{c[6]}"
+def _draw(case):
+    rng = np.random.default_rng(9000 + case)
+    cp = int(rng.choice([1, 2, 3, 4, 8]))
+    rank = int(rng.integers(0, cp))
+    hq, hkv, dqk, dv = HEADS[case % len(HEADS)]     # every layout six times
+    n = int(rng.integers(1, 7))
+    # chunk lengths from 1 token to a few hundred, total at most ~4k tokens
+    chunk = rng.choice([1, 2, 3, 8, 17, 40, 64, 100, 255], size=n)
+    lengths = [int(2 * cp * c) for c in chunk]
+    while sum(lengths) > 4096:
+        lengths.pop()
+    concurrency = int(rng.choice([0, 8, 64]))
+    return cp, rank, hq, hkv, dqk, dv, lengths, concurrency
 
 
-@pytest.mark.parametrize("case", GRID, ids=_ids)
-def test_edge_shapes_forward_and_backward(case):
-    seed, lengths, cp, rank, hq, hkv, dqk, dv = case
-    b = workloads.small_case(seed, lengths, cp, hq, hkv, dqk, dv, backward=True, rank=rank)
+@pytest.mark.parametrize("case", range(48))
+def test_random_shapes(case):
+    cp, rank, hq, hkv, dqk, dv, lengths, concurrency = _draw(case)
+    print(f"[sweep] case={case} cp={cp} rank={rank} hq={hq} hkv={hkv} dqk={dqk} dv={dv} "
+          f"lengths={lengths} concurrency={concurrency}", flush=True)
+    b = workloads.small_case(9000 + case, lengths, cp, hq, hkv, dqk, dv, backward=True, rank=rank)
     dev = device()
     q, k, v, do = (t.to(dev) for t in (b.q, b.k, b.v, b.do))
-    print(f"[sweep] seed={seed} lengths={lengths} cp={cp} rank={rank} hq={hq} hkv={hkv} "
-          f"dqk={dqk} dv={dv}", flush=True)
     want_o, want_lse = oatt.attn_fwd64(to64(b.q), to64(b.k), to64(b.v), lengths, cp, rank)
 
-    o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=lengths, cp=cp, rank=rank)
-    torch.cuda.synchronize()
-    assert_close(to64(o), want_o, "O")
-    assert_close(to64(lse), want_lse, "LSE", max_abs=LSE_ABS, mean_abs=LSE_ABS)
-
-    # As many work items as the planner will make: tiles with more than eight
-    # key tiles are cut into parts that the combine kernel merges.
-    o_s, lse_s = thd.attn_fwd(q=q, k=k, v=v, seqlens=lengths, cp=cp, rank=rank,
-                              concurrency=1 << 20)
-    torch.cuda.synchronize()
-    assert_close(to64(o_s), want_o, "O (split)")
-    assert_close(to64(lse_s), want_lse, "LSE (split)", max_abs=LSE_ABS, mean_abs=LSE_ABS)
-
-    o32 = torch.empty((q.shape[0], hq, dv), dtype=torch.float32, device=dev)
-    o_x, lse_x = thd.attn_fwd(q=q, k=k, v=v, seqlens=lengths, cp=cp, rank=rank, out_f32=o32)
-    torch.cuda.synchronize()
-    assert_close(to64(o32), want_o, "O32", max_abs=2e-4, mean_abs=2e-5)
-    assert_close(to64(lse_x), want_lse, "LSE (exact)", max_abs=LSE_ABS, mean_abs=LSE_ABS)
-
-    want = oatt.attn_bwd64(to64(b.q), to64(b.k), to64(b.v), to64(b.do), lengths, cp, rank)
-    for o_f32 in (None, o32):
-        got = thd.attn_bwd(q=q, k=k, v=v, lse=lse_x, d_o=do, seqlens=lengths, cp=cp, rank=rank,
-                           o_f32=o_f32)
+    # forward, plain plan (the batch's preferred tile sizes), then packed
+    for packed in (False, True):
+        meta = thd.device_metadata(seqlens=b.lengths, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=dqk,
+                                   d_v=dv, device=0, concurrency=concurrency, forward=True,
+                                   packed=packed)
+        o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=b.lengths, cp=cp, rank=rank, meta=meta)
         torch.cuda.synchronize()
-        path = "D from scores" if o_f32 is None else "D from O32"
+        assert_close(to64(o), want_o, f"O packed={packed}")
+        assert_close(lse.cpu().double().numpy(), want_lse, f"LSE packed={packed}",
+                     max_abs=LSE_ABS, mean_abs=LSE_ABS)
+
+    # backward, D from the scores and D from the exact fp32 O
+    want = oatt.attn_bwd64(to64(b.q), to64(b.k), to64(b.v), to64(b.do), lengths, cp, rank)
+    for exact_o in (False, True):
+        o32 = torch.empty((q.shape[0], hq, dv), dtype=torch.float32, device=dev) if exact_o else None
+        o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=b.lengths, cp=cp, rank=rank, out_f32=o32)
+        got = thd.attn_bwd(q=q, k=k, v=v, lse=lse, d_o=do, seqlens=b.lengths, cp=cp, rank=rank,
+                           o_f32=o32)
+        torch.cuda.synchronize()
         for name, g, e in zip(("dQ", "dK", "dV"), got, want):
-            assert_close(to64(g), e, f"{name} ({path})")
+            assert_close(g.cpu().double().numpy(), e, f"{name} exact_o={exact_o}")
+
+    # shard by shard, local shard first
+    bt, _ = thd.preferred_tiles(hq=hq, hkv=hkv, d_qk=dqk, d_v=dv)
+    order = [rank] + [s for s in range(cp) if s != rank]
+    state = None
+    for i, s in enumerate(order):
+        meta = thd.build_pass_metadata(seqlens=b.lengths, cp=cp, rank=rank, block_t=bt,
+                                       block_n=64, shards=[s], device=0)
+        if state is None:
+            state = thd.pass_state(meta=meta, hq=hq, hkv=hkv, d_v=dv, device=dev)
+        res = thd.attn_fwd_pass(q=q, k=k, v=v, meta=meta, state=state, first=i == 0,
+                                last=i == len(order) - 1)
+    torch.cuda.synchronize()
+    o, lse = res
+    assert_close(to64(o), want_o, "O shard by shard")
+    assert_close(lse.cpu().double().numpy(), want_lse, "LSE shard by shard",
+                 max_abs=LSE_ABS, mean_abs=LSE_ABS)
