@@ -354,6 +354,17 @@ int thd_build_pass_metadata(const int32_t* seqlens, int32_t n_docs, int32_t cp, 
                             int32_t block_t, int32_t block_n, uint64_t shard_mask,
                             int32_t device, thd_meta** out);
 
+/* thd_build_pass_metadata for the padded layout of real_lengths[n_docs] (host),
+ * as thd_build_metadata_padded is for thd_build_metadata: the pass plan of the
+ * padded lengths, plus DOC_END = cu_i + R_i, which the last pass reads to write
+ * pad rows as O = 0, LSE = +inf. Sources: as thd_build_pass_metadata, and the
+ * divisibility rule of "feat: kvallgather cp thd load balance #3820" ("Does
+ * this PR introduce any user-facing change?") relaxed by padding as in
+ * thd_pad_lengths. Errors as thd_build_pass_metadata and thd_pad_lengths. */
+int thd_build_pass_metadata_padded(const int32_t* real_lengths, int32_t n_docs, int32_t cp,
+                                   int32_t rank, int32_t block_t, int32_t block_n,
+                                   uint64_t shard_mask, int32_t device, thd_meta** out);
+
 /* Bytes of running state the passes of one forward share (the caller's;
  * fp32 O [T_local, Hq, d_v] then its base-2 log-sum-exp [T_local, Hq]). A
  * pass needs no other workspace. Source: as thd_build_pass_metadata.

@@ -92,6 +92,9 @@ def _load():
                                                 ctypes.c_float, p]),
         "thd_build_pass_metadata": (ctypes.c_int, [pi32, i32, i32, i32, i32, i32, ctypes.c_uint64,
                                                    i32, ctypes.POINTER(p)]),
+        "thd_build_pass_metadata_padded": (ctypes.c_int, [pi32, i32, i32, i32, i32, i32,
+                                                          ctypes.c_uint64, i32,
+                                                          ctypes.POINTER(p)]),
         "thd_attn_fwd_pass_state_bytes": (ctypes.c_int, [p, i32, i32, i32, pi64]),
         "thd_attn_fwd_pass": (ctypes.c_int, [p, p, p, p, p, p, p, i32, i32, i32, i32, i32,
                                              ctypes.c_float, p]),
@@ -112,7 +115,8 @@ EXPORTS = ("thd_last_error", "thd_plan_partition", "thd_build_metadata", "thd_pa
            "thd_meta_copy", "thd_meta_release", "thd_cache_stats", "thd_cache_clear",
            "thd_preferred_tiles", "thd_preferred_fwd_tiles", "thd_fwd_concurrency",
            "thd_attn_fwd_workspace", "thd_attn_fwd", "thd_attn_fwd_noalloc",
-           "thd_build_pass_metadata", "thd_attn_fwd_pass_state_bytes", "thd_attn_fwd_pass",
+           "thd_build_pass_metadata", "thd_build_pass_metadata_padded",
+           "thd_attn_fwd_pass_state_bytes", "thd_attn_fwd_pass",
            "thd_attn_bwd_workspace", "thd_attn_bwd")
 PASS_FIRST = 1
 PASS_LAST = 2
@@ -421,9 +425,10 @@ def attn_fwd(*, q, k, v, seqlens, cp: int, rank: int, softmax_scale=None, out=No
 
 
 def build_pass_metadata(*, seqlens, cp: int, rank: int, block_t: int, block_n: int, shards,
-                        device: int = -1) -> Meta:
+                        device: int = -1, padded: bool = False) -> Meta:
     """Metadata of one forward pass over the keys of the listed source ranks'
-    shards (all-gather overlap; thd_build_pass_metadata)."""
+    shards (all-gather overlap; thd_build_pass_metadata). padded: seqlens are
+    real lengths and the tensors use the padded layout (as build_metadata)."""
     lens = _lengths(seqlens)
     mask = 0
     for s_ in shards:
@@ -432,8 +437,8 @@ def build_pass_metadata(*, seqlens, cp: int, rank: int, block_t: int, block_n: i
             raise ThdError(-1, "shard ranks must lie in [0, 64)")
         mask |= 1 << s_
     h = ctypes.c_void_p()
-    _check(_lib.thd_build_pass_metadata(_ptr32(lens), len(lens), cp, rank, block_t, block_n,
-                                        mask, device, ctypes.byref(h)))
+    fn = _lib.thd_build_pass_metadata_padded if padded else _lib.thd_build_pass_metadata
+    _check(fn(_ptr32(lens), len(lens), cp, rank, block_t, block_n, mask, device, ctypes.byref(h)))
     return Meta(h)
 
 

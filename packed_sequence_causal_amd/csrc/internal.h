@@ -66,10 +66,10 @@ std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t
 
 // The plan of one forward pass over the keys held by the source ranks in
 // shard_mask (bit s = rank s's shard): same tiles, items over maximal runs of
-// such chunks (see build_pass_plan).
+// such chunks (see build_pass_plan). real_lengths as for build_plan.
 std::unique_ptr<Plan> build_pass_plan(const int32_t* seqlens, int32_t n_docs, int32_t cp,
                                       int32_t rank, int32_t block_t, int32_t block_n,
-                                      uint64_t shard_mask);
+                                      uint64_t shard_mask, const int32_t* real_lengths);
 
 // Device copies of the arrays the kernels read.
 struct DeviceMeta {

@@ -244,7 +244,7 @@ void build_metadata_impl(const int32_t* seqlens, const int32_t* real, int32_t n_
   } else {
     ++c.misses;
     auto e = std::make_shared<MetaEntry>();
-    e->plan = pass ? build_pass_plan(seqlens, n_docs, cp, rank, block_t, block_n, shard_mask)
+    e->plan = pass ? build_pass_plan(seqlens, n_docs, cp, rank, block_t, block_n, shard_mask, real)
                    : build_plan(seqlens, n_docs, cp, rank, block_t, block_n, concurrency, real,
                                 packed);
     if (device >= 0) {
@@ -625,6 +625,20 @@ int thd_build_pass_metadata(const int32_t* seqlens, int32_t n_docs, int32_t cp, 
   return guarded([&] {
     build_metadata_impl(seqlens, nullptr, n_docs, cp, rank, block_t, block_n, 0, device, out,
                         true, shard_mask);
+  });
+}
+
+int thd_build_pass_metadata_padded(const int32_t* real_lengths, int32_t n_docs, int32_t cp,
+                                   int32_t rank, int32_t block_t, int32_t block_n,
+                                   uint64_t shard_mask, int32_t device, thd_meta** out) {
+  return guarded([&] {
+    if (out == nullptr) fail(THD_EINVAL, "out is NULL");
+    *out = nullptr;
+    if (n_docs < 1) fail(THD_EINVAL, "n_docs must be >= 1");
+    std::vector<int32_t> padded(n_docs);
+    pad_lengths(real_lengths, n_docs, cp, padded.data());
+    build_metadata_impl(padded.data(), real_lengths, n_docs, cp, rank, block_t, block_n, 0,
+                        device, out, true, shard_mask);
   });
 }
 

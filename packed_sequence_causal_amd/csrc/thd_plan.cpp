@@ -316,12 +316,12 @@ std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t
 
 std::unique_ptr<Plan> build_pass_plan(const int32_t* seqlens, int32_t n_docs, int32_t cp,
                                       int32_t rank, int32_t block_t, int32_t block_n,
-                                      uint64_t shard_mask) {
+                                      uint64_t shard_mask, const int32_t* real_lengths) {
   validate_partition(seqlens, n_docs, cp, rank);
   if (cp > 64) fail(THD_ERANGE, "pass plans take cp <= 64 (one mask bit per source rank)");
   if (shard_mask == 0 || (cp < 64 && (shard_mask >> cp) != 0))
     fail(THD_EINVAL, "shard_mask must name at least one source rank, and only ranks < cp");
-  auto plan = build_plan(seqlens, n_docs, cp, rank, block_t, block_n, 0, nullptr);
+  auto plan = build_plan(seqlens, n_docs, cp, rank, block_t, block_n, 0, real_lengths);
   Plan& p = *plan;
   p.pass = true;
   p.shard_mask = shard_mask;

@@ -18,7 +18,7 @@
 
 namespace {
 
-enum Kind { kPlain, kPacked, kPackedPadded, kPass };
+enum Kind { kPlain, kPacked, kPackedPadded, kPass, kPassPadded };
 
 struct Case {
   std::vector<int32_t> lengths;
@@ -39,6 +39,9 @@ int build(const Case& c, thd_meta** m) {
     case kPass:
       return thd_build_pass_metadata(c.lengths.data(), n, c.cp, c.rank, c.block_t, c.block_n,
                                      c.shards, -1, m);
+    case kPassPadded:
+      return thd_build_pass_metadata_padded(c.lengths.data(), n, c.cp, c.rank, c.block_t,
+                                            c.block_n, c.shards, -1, m);
     default:
       return thd_build_metadata(c.lengths.data(), n, c.cp, c.rank, c.block_t, c.block_n,
                                 c.concurrency, -1, m);
@@ -99,6 +102,7 @@ int main() {
       {{5, 13, 8, 3, 30, 1, 22}, 2, 0, 32, 64, 0, kPackedPadded},
       {{16, 32, 1040, 16, 400}, 8, 3, 32, 64, 0, kPass, 0x9u},
       {{256, 512, 256}, 2, 1, 64, 64, 0, kPass, 0x2u},
+      {{17, 1040, 9, 400}, 8, 3, 32, 64, 0, kPassPadded, 0x11u},
   };
   std::vector<Snapshot> ref;
   for (const Case& c : cases) {

@@ -93,3 +93,36 @@ def test_padded_backward_matches_oracle(case, exact_o):
     assert np.all(got[1][pad_keys] == 0.0) and np.all(got[2][pad_keys] == 0.0)
     for name, g, e in zip(("dQ", "dK", "dV"), got, want):
         assert_close(g, e, f"padded {name}")
+
+
+@pytest.mark.parametrize("case", CASES, ids=lambda c: f"seed{c[0]}")
+def test_padded_shard_passes_match_oracle(case):
+    """Padded layout, forward run shard by shard (local shard first) through
+    the running state: real rows match the oracle, and the last pass writes
+    pad rows as O = 0, LSE = +inf."""
+    seed, real, cp, rank, hq, hkv, dqk, dv = case
+    b = _batch(case)
+    dev = device()
+    q, k, v = b.q.to(dev), b.k.to(dev), b.v.to(dev)
+    print(f"[pad passes] seed={seed} real={real} cp={cp} rank={rank}", flush=True)
+    bt, _ = thd.preferred_tiles(hq=hq, hkv=hkv, d_qk=dqk, d_v=dv)
+    order = [rank] + [s for s in range(cp) if s != rank]
+    state = None
+    for i, s in enumerate(order):
+        meta = thd.build_pass_metadata(seqlens=real, cp=cp, rank=rank, block_t=bt, block_n=64,
+                                       shards=[s], device=0, padded=True)
+        if state is None:
+            state = thd.pass_state(meta=meta, hq=hq, hkv=hkv, d_v=dv, device=dev)
+        res = thd.attn_fwd_pass(q=q, k=k, v=v, meta=meta, state=state, first=i == 0,
+                                last=i == len(order) - 1)
+    torch.cuda.synchronize()
+    o, lse = res
+    want_o, want_lse = oatt.attn_fwd64_padded(to64(b.q), to64(b.k), to64(b.v), real, cp, rank)
+    pad = opart.pad_rows(real, cp, rank)
+    got_o = to64(o)
+    got_lse = lse.cpu().double().numpy()
+    assert pad.any()
+    assert np.all(got_o[pad] == 0.0)
+    assert np.all(np.isposinf(got_lse[pad]))
+    assert_close(got_o[~pad], want_o[~pad], "O")
+    assert_close(got_lse[~pad], want_lse[~pad], "LSE", max_abs=LSE_ABS, mean_abs=LSE_ABS)

@@ -3,7 +3,7 @@
 Hypothesis draws context-parallel sizes, ranks, document lengths (real lengths
 of any size, padded to multiples of 2cp where a plan takes them), tile sizes,
 split concurrencies and shard sets, and every plan kind the library builds
-(plain, padded, packed, packed padded, shard pass) must equal the oracle's
+(plain, padded, packed, packed padded, shard pass, padded shard pass) must equal the oracle's
 tables bit for bit. The draws are derandomised, so a run is reproducible.
 """
 import numpy as np
@@ -99,6 +99,13 @@ def test_pass_plans(problem, bt, data):
     assert np.array_equal(m.field("splits"), want_tiles)
     assert np.array_equal(m.field("tiles"), ometa.tiles(lengths, cp, rank, bt, 64))
     assert m.info()["shard_mask"] == sum(1 << s for s in shards)
+    # the padded pass plan of the real lengths: the same tables, real document ends
+    mp = thd.build_pass_metadata(seqlens=real, cp=cp, rank=rank, block_t=bt, block_n=64,
+                                 shards=shards, padded=True)
+    for name in ("q_global", "kv_row", "tiles", "items", "splits"):
+        assert np.array_equal(mp.field(name), m.field(name)), name
+    assert np.array_equal(mp.field("doc_end"), ometa.doc_end(lengths, cp, real))
+    assert mp.info()["is_pass"] == 1 and mp.info()["pad_tokens"] == sum(lengths) - sum(real)
 
 
 @pytest.mark.parametrize("cp", [1, 3, 8])
