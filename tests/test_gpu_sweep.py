@@ -6,7 +6,8 @@ lengths (from a single token per chunk up to several KV tiles), a head layout
 checks on every element: the forward (the plan's own tiles), the packed-plan
 forward, the backward on both D paths, and a forward run shard by shard.
 The draws come from numpy's generator seeded by the case number, so every
-case is fixed and printed before it runs.
+case is fixed and printed before it runs. Fixed cases with 32 to 128 q heads
+per kv head (query tiles of 4 tokens down to one) follow.
 """
 import numpy as np
 import pytest
@@ -87,3 +88,41 @@ def test_random_shapes(case):
     assert_close(to64(o), want_o, "O shard by shard")
     assert_close(lse.cpu().double().numpy(), want_lse, "LSE shard by shard",
                  max_abs=LSE_ABS, mean_abs=LSE_ABS)
+
+
+LARGE_GROUPS = [
+    # (seed, lengths, cp, rank, hq, hkv, dqk, dv): 32 to 128 q heads per kv head,
+    # so a query tile holds 4 tokens down to a single one, and dK, dV sum over
+    # that many heads
+    (9101, [64, 200, 40], 2, 1, 32, 1, 128, 128),
+    (9102, [16, 96, 8, 48], 4, 2, 64, 1, 64, 64),
+    (9103, [24, 120, 8], 2, 0, 128, 1, 128, 128),
+    (9104, [48, 16, 80], 4, 3, 128, 2, 128, 128),
+    (9105, [32, 96], 2, 1, 64, 1, 192, 128),
+]
+
+
+@pytest.mark.parametrize("case", LARGE_GROUPS, ids=lambda c: f"seed{c[0]}")
+def test_large_groups(case):
+    seed, lengths, cp, rank, hq, hkv, dqk, dv = case
+    print(f"[large groups] seed={seed} G={hq // hkv} lengths={lengths} cp={cp} rank={rank} "
+          f"dqk={dqk}", flush=True)
+    b = workloads.small_case(seed, lengths, cp, hq, hkv, dqk, dv, backward=True, rank=rank)
+    dev = device()
+    q, k, v, do = (t.to(dev) for t in (b.q, b.k, b.v, b.do))
+    want_o, want_lse = oatt.attn_fwd64(to64(b.q), to64(b.k), to64(b.v), lengths, cp, rank)
+    for packed in (False, True):
+        o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=b.lengths, cp=cp, rank=rank, packed=packed)
+        torch.cuda.synchronize()
+        assert_close(to64(o), want_o, f"O packed={packed}")
+        assert_close(lse.cpu().double().numpy(), want_lse, f"LSE packed={packed}",
+                     max_abs=LSE_ABS, mean_abs=LSE_ABS)
+    want = oatt.attn_bwd64(to64(b.q), to64(b.k), to64(b.v), to64(b.do), lengths, cp, rank)
+    for exact_o in (False, True):
+        o32 = torch.empty((q.shape[0], hq, dv), dtype=torch.float32, device=dev) if exact_o else None
+        o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=b.lengths, cp=cp, rank=rank, out_f32=o32)
+        got = thd.attn_bwd(q=q, k=k, v=v, lse=lse, d_o=do, seqlens=b.lengths, cp=cp, rank=rank,
+                           o_f32=o32)
+        torch.cuda.synchronize()
+        for name, g, e in zip(("dQ", "dK", "dV"), got, want):
+            assert_close(g.cpu().double().numpy(), e, f"{name} exact_o={exact_o}")
