@@ -43,6 +43,10 @@ struct Plan {
   // backward key tiles.
   bool packed = false;
   int64_t n_packed = 0;
+  // For the dK/dV kernel: the key tiles ordered by how many local query
+  // tokens see them, most first (stable), so the longest workgroups start
+  // first (a scheduling choice; every key tile writes only its own rows).
+  std::vector<int32_t> kv_order;
   std::vector<int32_t> q_global, kv_row, chunk_off, tiles, order, kvtiles, items, splits, doc_end;
   std::vector<int32_t> pack_rows, pack_keys;
   int item_ints() const { return pass ? 8 : 4; }
@@ -87,6 +91,7 @@ struct DeviceMeta {
   const int32_t* pack_keys = nullptr;
   const int32_t* pass_runs = nullptr;
   const int32_t* pass_order = nullptr;
+  const int32_t* kv_order = nullptr;
 };
 
 struct MetaEntry {
@@ -189,7 +194,9 @@ struct BwdParams {
   float* delta;       // workspace: D [T_local, Hq]
   float* lse2;        // workspace: lse * log2(e) [T_local, Hq]
   const int32_t* tiles;
+  const int32_t* order;      // dQ workgroup b takes query tile order[b / hkv] (largest first)
   const int32_t* kvtiles;
+  const int32_t* kv_order;   // dK/dV workgroup b takes key tile kv_order[b / hkv]
   const int32_t* kv_row;
   int32_t n_tiles, n_kvtiles, hq, hkv, group, block_t;
   int64_t total, local;

@@ -64,11 +64,12 @@ struct DeviceScope {
 void upload(MetaEntry& e, int device) {
   const Plan& p = *e.plan;
   DeviceScope scope(device);
-  constexpr int kParts = 12;
+  constexpr int kParts = 13;
   const std::vector<int32_t>* parts[kParts] = {&p.kv_row,    &p.tiles,     &p.order,
                                                &p.kvtiles,   &p.q_global,  &p.items,
                                                &p.splits,    &p.doc_end,   &p.pack_rows,
-                                               &p.pack_keys, &p.pass_runs, &p.pass_order};
+                                               &p.pack_keys, &p.pass_runs, &p.pass_order,
+                                               &p.kv_order};
   size_t offs[kParts];
   size_t bytes = 0;
   for (int i = 0; i < kParts; ++i) {
@@ -101,6 +102,7 @@ void upload(MetaEntry& e, int device) {
   e.dev.pack_keys = reinterpret_cast<const int32_t*>(b + offs[9]);
   e.dev.pass_runs = reinterpret_cast<const int32_t*>(b + offs[10]);
   e.dev.pass_order = reinterpret_cast<const int32_t*>(b + offs[11]);
+  e.dev.kv_order = reinterpret_cast<const int32_t*>(b + offs[12]);
 }
 
 // Least-recently-used cache of metadata entries. Entries still referenced by a
@@ -779,7 +781,9 @@ int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void*
     bp.delta = static_cast<float*>(workspace);
     bp.lse2 = reinterpret_cast<float*>(static_cast<char*>(workspace) + bwd_ws_array_bytes(p.local, hq));
     bp.tiles = d.tiles;
+    bp.order = d.order;
     bp.kvtiles = d.kvtiles;
+    bp.kv_order = d.kv_order;
     bp.kv_row = d.kv_row;
     bp.n_tiles = int32_t(n_tiles);
     bp.n_kvtiles = int32_t(n_kvtiles);

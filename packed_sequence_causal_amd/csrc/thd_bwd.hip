@@ -38,6 +38,10 @@
 //      and dS^T, so dV += P^T dO and dK += dS^T Q take their B operands from
 //      the row-major dO and Q blocks with transpose reads. Tiles no local
 //      query sees write zeros.
+// Dispatch order: dQ-kernel workgroups take query tiles in the plan's order
+// (most KV tiles first), dK/dV workgroups key tiles by the local query tokens
+// that see them (most first). Each workgroup writes only its own rows, so the
+// order changes no result, only how evenly the CUs finish.
 #include <hip/hip_runtime.h>
 
 #include <climits>
@@ -154,7 +158,9 @@ __global__ __launch_bounds__(kWaves * 64, DQK > 128 ? 1 : 2) void thd_bwd_dq_ker
   const int lrow = lane & 31;
 
   const int kvh = blockIdx.x % p.hkv;
-  const int tile = blockIdx.x / p.hkv;
+  // Query tiles go out with the most KV tiles first (the plan's order), as
+  // in the forward, so the longest walks do not start last.
+  const int tile = ((const cint32_t*)p.order)[blockIdx.x / p.hkv];
   const int32_t* td = p.tiles + size_t(tile) * 8;
   const int q_local0 = td[0], q_glob0 = td[1], n_rows = td[2], kv_start = td[5];
   const int n_kv = td[6], n_full = td[7];
@@ -496,7 +502,9 @@ __global__ __launch_bounds__(kDkvWaves * 64, DQK > 128 ? 2 : 3) void thd_bwd_dkd
   const int lr = lane & 15;
 
   const int kvh = blockIdx.x % p.hkv;
-  const int kt = blockIdx.x / p.hkv;
+  // Key tiles go out most-seen first (kv_order), so the longest walks start
+  // first and the short ones fill in at the end.
+  const int kt = ((const cint32_t*)p.kv_order)[blockIdx.x / p.hkv];
   // The tables are read-only for the whole launch: reading them through the
   // constant address space lets uniform reads use scalar loads.
   const cint32_t* kd = (const cint32_t*)(p.kvtiles) + size_t(kt) * 8;

@@ -269,6 +269,19 @@ std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t
     }
     cu += seqlens[i];
   }
+  // The dK/dV kernel's dispatch order: key tiles by the local query tokens
+  // that see them (their query tiles' rows), most first, stable.
+  {
+    const int64_t n_kv = int64_t(p.kvtiles.size() / 8);
+    std::vector<int64_t> seen(size_t(n_kv), 0);
+    for (int64_t j = 0; j < n_kv; ++j)
+      for (int32_t t = p.kvtiles[size_t(j) * 8 + 3]; t < p.kvtiles[size_t(j) * 8 + 4]; ++t)
+        seen[size_t(j)] += p.tiles[size_t(t) * 8 + 2];
+    p.kv_order.resize(size_t(n_kv));
+    std::iota(p.kv_order.begin(), p.kv_order.end(), 0);
+    std::stable_sort(p.kv_order.begin(), p.kv_order.end(),
+                     [&](int32_t a, int32_t b) { return seen[size_t(a)] > seen[size_t(b)]; });
+  }
   // Forward work items: the key range of the longest tiles is cut into parts
   // when the tiles alone are too few to keep the device busy, so no single
   // workgroup's loop is much longer than the average per workgroup slot. Every
