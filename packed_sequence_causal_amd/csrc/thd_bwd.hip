@@ -609,11 +609,22 @@ __global__ __launch_bounds__(kDkvWaves * 64, DQK > 128 ? 2 : 3) void thd_bwd_dkd
       const size_t rb = b.base + size_t(b.sb * tokens_per_block) * hq;
       const char* qt = qbase + rb * S::KROWB;
       const char* ot = obase + rb * S::VROWB;
+      // The offsets pass through an empty asm so that they stay 32-bit
+      // registers: the compiler would otherwise keep 64-bit copies across the
+      // walk and spill them at d_qk = 192 (every reload then waits for all
+      // copies in flight).
 #pragma unroll
-      for (int i = 0; i < S::Q_IPW; ++i) load_lds16(qt + qoff[i], stage + (wave * S::Q_IPW + i) * 1024);
+      for (int i = 0; i < S::Q_IPW; ++i) {
+        uint32_t off = qoff[i];
+        asm volatile("" : "+v"(off));
+        load_lds16(qt + off, stage + (wave * S::Q_IPW + i) * 1024);
+      }
 #pragma unroll
-      for (int i = 0; i < S::O_IPW; ++i)
-        load_lds16(ot + ooff[i], stage + S::QBYTES + (wave * S::O_IPW + i) * 1024);
+      for (int i = 0; i < S::O_IPW; ++i) {
+        uint32_t off = ooff[i];
+        asm volatile("" : "+v"(off));
+        load_lds16(ot + off, stage + S::QBYTES + (wave * S::O_IPW + i) * 1024);
+      }
       // gathered straight into LDS: a register load here would have to wait
       // for every copy issued before it
       if (wave < 2 && lane < kRowsPerBlock) load_lds4(reinterpret_cast<const char*>(info + rb + ioff), info_lds);
@@ -621,16 +632,21 @@ __global__ __launch_bounds__(kDkvWaves * 64, DQK > 128 ? 2 : 3) void thd_bwd_dkd
     }
     const char* qt = qbase + b.base * S::KROWB;
     const char* ot = obase + b.base * S::VROWB;
+    // The lane's chunk offsets are recomputed from an opaque copy of the lane
+    // id: kept live across the walk instead, they spill at d_qk = 192, and
+    // every reload of a spill waits for all copies in flight.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
 #pragma unroll
     for (int i = 0; i < S::Q_IPW; ++i) {
-      const int q = (wave * S::Q_IPW + i) * 64 + lane;
+      const int q = (wave * S::Q_IPW + i) * 64 + ln;
       const int r = q / S::KCPR;
       const int c = (q - r * S::KCPR) ^ swz_kv<S::KCPR>(r);
       load_lds16(qt + (row_off(b, r) * S::KROWB + c * 16), stage + (wave * S::Q_IPW + i) * 1024);
     }
 #pragma unroll
     for (int i = 0; i < S::O_IPW; ++i) {
-      const int q = (wave * S::O_IPW + i) * 64 + lane;
+      const int q = (wave * S::O_IPW + i) * 64 + ln;
       const int r = q / S::VCPR;
       const int c = (q - r * S::VCPR) ^ swz_kv<S::VCPR>(r);
       load_lds16(ot + (row_off(b, r) * S::VROWB + c * 16), stage + S::QBYTES + (wave * S::O_IPW + i) * 1024);
