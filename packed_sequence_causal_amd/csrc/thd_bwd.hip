@@ -147,8 +147,11 @@ struct DqShape {
   }
 };
 
+// Two workgroups per CU, except the d_qk = 192 dQ pass: its Q and dO
+// fragments, six dQ accumulators and the S and dP tiles need about 430
+// registers (one workgroup per CU). Its D pass, without dQ, fits two.
 template <int DQK, int DV, bool DELTA>
-__global__ __launch_bounds__(kWaves * 64, DQK > 128 ? 1 : 2) void thd_bwd_dq_kernel(BwdParams p) {
+__global__ __launch_bounds__(kWaves * 64, DQK > 128 && !DELTA ? 1 : 2) void thd_bwd_dq_kernel(BwdParams p) {
   using S = DqShape<DQK, DV>;
   __shared__ __attribute__((aligned(1024))) char smem[2 * S::STAGE];
   const int tid = threadIdx.x;
