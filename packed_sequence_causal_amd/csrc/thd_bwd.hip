@@ -536,6 +536,9 @@ __global__ __launch_bounds__(kDkvWaves * 64, DQK > 128 ? 2 : 3) void thd_bwd_dkd
     for (int st = 0; st < S::KS; ++st) kf[st] = *reinterpret_cast<const bf16x8*>(krow + 32 * st);
 #pragma unroll
     for (int st = 0; st < S::VS; ++st) vf[st] = *reinterpret_cast<const bf16x8*>(vrow + 32 * st);
+    // Landed before the walk: pending at the loop's entry, these loads would
+    // make the compiler wait for every copy in flight inside the loop.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   } else {
 #pragma unroll
     for (int st = 0; st < S::KS; ++st) kf[st] = bf16x8{};
@@ -555,6 +558,10 @@ __global__ __launch_bounds__(kDkvWaves * 64, DQK > 128 ? 2 : 3) void thd_bwd_dkd
       rec_qg = td[1];
       rec_nr = td[2];
     }
+    // Resolved here, on this rare path: otherwise the compiler cannot tell
+    // at the walk's merge points whether these loads are still in flight,
+    // and waits for every copy in flight before each tile's readlanes.
+    __builtin_amdgcn_s_waitcnt(0x0F70);   // vmcnt(0)
   };
   if (qb < qe) load_window(qb);
   auto load_tile = [&](int t) -> RowBlock {
