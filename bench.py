@@ -78,9 +78,10 @@ def _kernel_sha() -> str:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
-def _traffic(workload: str):
+def _traffic(workload: str, block_n: int):
     """HBM bytes per forward launch from the committed counter summary, if it
-    was taken on the current kernel source; else None."""
+    was taken on the current kernel source and on the KV tile size this run
+    uses; else None."""
     path = os.path.join(ROOT, "profiles", f"thd_fwd_kernel_{workload}_counters.md")
     if not os.path.exists(path):
         return None
@@ -91,6 +92,8 @@ def _traffic(workload: str):
                 key, val = line[2:].split(":", 1)
                 fields[key.strip()] = val.strip().strip("`")
     if fields.get("kernel_source_sha256") != _kernel_sha():
+        return None
+    if fields.get("kernel_block_n") != str(block_n):
         return None
     try:
         return float(fields["hbm_bytes_per_launch"])
@@ -383,7 +386,7 @@ def measure(w, args, dev, cpu_budget_s: float):
                 "peak": PEAK_HBM_GBS, "unit": "GB/s"}
     roof["frac"] = round(roof["achieved"] / roof["peak"], 4)
     kernels = "thd_fwd_kernel" + (" + thd_fwd_combine_kernel" if info["n_splits"] > 0 else "")
-    roof.update({"traffic": _traffic(w.name), "kernel": kernels, "kernel_ms": round(kern_ms, 5),
+    roof.update({"traffic": _traffic(w.name, int(info["block_n"])), "kernel": kernels, "kernel_ms": round(kern_ms, 5),
                  "algorithmic_bytes": int(alg_bytes), "useful_flops": int(fwd_flops),
                  "intensity_flop_per_byte": round(intensity, 1),
                  "mfma_frac": round(fwd_flops / (kern_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4)})

@@ -264,13 +264,18 @@ int thd_preferred_tiles(int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
  * They are chosen (block_n = 32) when they compute at least 7% fewer key
  * slots than 64-key tiles: a query tile visits its document's keys up to its
  * last row, rounded up to whole KV tiles, so short chunks leave most of a
- * 64-key tile masked. Otherwise block_n = 64. block_t as thd_preferred_tiles.
- * Metadata built with block_n = 32 serves thd_attn_fwd only: thd_attn_bwd
- * needs block_n = 64 (THD_EMISMATCH otherwise). Errors as
- * thd_plan_partition, plus THD_EUNSUPPORTED. */
+ * 64-key tile masked. They are also chosen when concurrency32 > 0 (the
+ * device's thd_fwd_concurrency for block_n = 32; 0 skips this rule), query
+ * tiles hold at most 32 tokens (Hq/Hkv >= 4) and the batch has at least
+ * 2 * concurrency32 query tiles, so that no tile's key range is split: a
+ * large grid of short query tiles then gains from the third workgroup per CU.
+ * Otherwise block_n = 64. block_t as thd_preferred_tiles. Metadata built with
+ * block_n = 32 serves thd_attn_fwd only: thd_attn_bwd needs block_n = 64
+ * (THD_EMISMATCH otherwise). Errors as thd_plan_partition, plus
+ * THD_EUNSUPPORTED and THD_EINVAL (concurrency32 < 0). */
 int thd_preferred_fwd_tiles(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank,
-                            int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v, int32_t* block_t,
-                            int32_t* block_n);
+                            int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
+                            int32_t concurrency32, int32_t* block_t, int32_t* block_n);
 
 /* Scheduling input of this library's planner (no page passage; it balances
  * the single fused forward call of "feat: kvallgather cp thd load balance

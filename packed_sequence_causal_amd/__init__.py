@@ -82,8 +82,8 @@ def _load():
         "thd_cache_stats": (ctypes.c_int, [pi64, pi64, pi64, pi64]),
         "thd_cache_clear": (ctypes.c_int, []),
         "thd_preferred_tiles": (ctypes.c_int, [i32, i32, i32, i32, pi32, pi32]),
-        "thd_preferred_fwd_tiles": (ctypes.c_int, [pi32, i32, i32, i32, i32, i32, i32, i32, pi32,
-                                                   pi32]),
+        "thd_preferred_fwd_tiles": (ctypes.c_int, [pi32, i32, i32, i32, i32, i32, i32, i32, i32,
+                                                   pi32, pi32]),
         "thd_fwd_concurrency": (ctypes.c_int, [i32, i32, i32, pi32]),
         "thd_attn_fwd_workspace": (ctypes.c_int, [p, i32, i32, i32, pi64]),
         "thd_attn_fwd": (ctypes.c_int, [p, p, p, p, p, p, p, i32, i32, i32, i32, ctypes.c_float, p,
@@ -294,14 +294,19 @@ _CONCURRENCY = {}
 
 
 def preferred_fwd_tiles(*, seqlens, cp: int, rank: int, hq: int, hkv: int, d_qk: int, d_v: int,
-                        padded: bool = False) -> tuple[int, int]:
+                        padded: bool = False, device: int | None = None,
+                        concurrency32: int | None = None) -> tuple[int, int]:
     """Forward tile sizes for this batch (thd_preferred_fwd_tiles): 32-key
     tiles when d_qk <= 128 and they compute at least 7% fewer key slots than
-    64-key tiles (query tiles visit whole KV tiles up to their last row)."""
+    64-key tiles (query tiles visit whole KV tiles up to their last row), or,
+    given the device (or its 32-key concurrency), when query tiles hold at most
+    32 tokens and there are enough of them that no key range is split."""
     lens = pad_lengths(seqlens=seqlens, cp=cp) if padded else _lengths(seqlens)
+    if concurrency32 is None:
+        concurrency32 = 0 if device is None else device_concurrency(device, hkv, 32)
     bt, bn = ctypes.c_int32(), ctypes.c_int32()
     _check(_lib.thd_preferred_fwd_tiles(_ptr32(lens), len(lens), cp, rank, hq, hkv, d_qk, d_v,
-                                        ctypes.byref(bt), ctypes.byref(bn)))
+                                        concurrency32, ctypes.byref(bt), ctypes.byref(bn)))
     return bt.value, bn.value
 
 
@@ -326,7 +331,7 @@ def device_metadata(*, seqlens, cp: int, rank: int, hq: int, hkv: int, d_qk: int
         raise ThdError(-1, "packed plans are forward-only: pass forward=True")
     if forward:
         bt, bn = preferred_fwd_tiles(seqlens=seqlens, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=d_qk,
-                                     d_v=d_v, padded=padded)
+                                     d_v=d_v, padded=padded, device=device)
     else:
         bt, bn = preferred_tiles(hq=hq, hkv=hkv, d_qk=d_qk, d_v=d_v)
     if concurrency is None:

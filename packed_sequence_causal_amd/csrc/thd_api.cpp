@@ -449,8 +449,8 @@ int thd_preferred_tiles(int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v, int3
 }
 
 int thd_preferred_fwd_tiles(const int32_t* seqlens, int32_t n_docs, int32_t cp, int32_t rank,
-                            int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v, int32_t* block_t,
-                            int32_t* block_n) {
+                            int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
+                            int32_t concurrency32, int32_t* block_t, int32_t* block_n) {
   return guarded([&] {
     validate_partition(seqlens, n_docs, cp, rank);
     check_heads(hq, hkv);
@@ -458,14 +458,21 @@ int thd_preferred_fwd_tiles(const int32_t* seqlens, int32_t n_docs, int32_t cp, 
       fail(THD_EUNSUPPORTED, "no kernel for d_qk=" + std::to_string(d_qk) +
                                  ", d_v=" + std::to_string(d_v));
     if (block_t == nullptr || block_n == nullptr) fail(THD_EINVAL, "output pointer is NULL");
+    if (concurrency32 < 0) fail(THD_EINVAL, "concurrency32 must be >= 0");
     // Key slots the forward computes (visited KV tiles times their size) with
     // 64- and with 32-key tiles: query tile t0.. of chunk k sees the document's
     // keys up to k*c + t0 + rows. Short tiles pay when they drop more than 7%
     // of the slots (keys past each tile's last row that a 64-key tile still
     // computes); below that their extra barriers and the tighter register
     // budget of the third workgroup cost more than they save.
+    // Second rule, when the caller gives the 32-key concurrency
+    // (thd_fwd_concurrency): query tiles of at most 32 tokens (four or more q
+    // heads per kv head) in a grid large enough that 32-key tiles need no
+    // split (at least two work items per slot). There the third workgroup per
+    // CU pays even without saved slots: 3-5% on GQA batches of 266 to 1050
+    // tiles, in both P paths, where MHA's 128-token tiles lose 10-18%.
     const int32_t bt = preferred_block_t(hq / hkv);
-    int64_t slots64 = 0, slots32 = 0;
+    int64_t slots64 = 0, slots32 = 0, n_tiles = 0;
     for (int32_t i = 0; i < n_docs; ++i) {
       const int64_t c = seqlens[i] / (2 * cp);
       for (int s = 0; s < 2; ++s) {
@@ -474,11 +481,14 @@ int thd_preferred_fwd_tiles(const int32_t* seqlens, int32_t n_docs, int32_t cp, 
           const int64_t kv_len = k * c + t0 + std::min<int64_t>(bt, c - t0);
           slots64 += (kv_len + kBlockN - 1) / kBlockN * kBlockN;
           slots32 += (kv_len + kBlockNShort - 1) / kBlockNShort * kBlockNShort;
+          ++n_tiles;
         }
       }
     }
+    const bool saves_slots = 100 * slots32 <= 93 * slots64;
+    const bool large_grid = concurrency32 > 0 && bt <= 32 && n_tiles >= 2 * int64_t(concurrency32);
     *block_t = bt;
-    *block_n = fwd_block_n_supported(d_qk, kBlockNShort) && 100 * slots32 <= 93 * slots64
+    *block_n = fwd_block_n_supported(d_qk, kBlockNShort) && (saves_slots || large_grid)
                    ? kBlockNShort
                    : kBlockN;
   });

@@ -152,6 +152,41 @@ def test_preferred_fwd_tiles_pick_short_tiles_when_they_save_key_slots():
     assert err.value.status == "THD_ENOTDIV"
 
 
+def test_preferred_fwd_tiles_take_short_tiles_for_large_grids_of_short_query_tiles():
+    """Given the 32-key concurrency C, 32-key tiles also when query tiles hold
+    at most 32 tokens (4+ q heads per kv head) and there are at least 2C of
+    them (no key range would be split); never for longer query tiles."""
+    rng = np.random.default_rng(78)
+    for _ in range(40):
+        cp = int(rng.choice([1, 2, 4, 8]))
+        lengths = workloads.random_lengths(rng, int(rng.integers(1, 12)), cp, 48)
+        rank = int(rng.integers(0, cp))
+        g = int(rng.choice([1, 2, 4, 8]))
+        bt = 128 // g
+        conc = int(rng.choice([1, 4, 16, 84]))
+        n_tiles = ometa.tiles(lengths, cp, rank, bt, 64).shape[0]
+        saves = 100 * _key_slots(lengths, cp, rank, bt, 32) <= 93 * _key_slots(
+            lengths, cp, rank, bt, 64)
+        want = 32 if saves or (bt <= 32 and n_tiles >= 2 * conc) else 64
+        got = thd.preferred_fwd_tiles(seqlens=lengths, cp=cp, rank=rank, hq=8 * g, hkv=8,
+                                      d_qk=128, d_v=128, concurrency32=conc)
+        assert got == (bt, want), (lengths, cp, rank, g, conc)
+    # the training workload (272 tiles of 32 tokens) at the 32-key concurrency
+    # of 256 CUs, three workgroups each, 7/8, over 8 kv heads: 32-key tiles;
+    # gqa_mid (134 tiles) would split them and keeps 64
+    conc = 256 * 3 * 7 // (8 * 8)
+    for name, bn in (("fwdbwd", 32), ("gqa_mid", 64), ("short", 32), ("mla", 64)):
+        w = workloads.BY_NAME[name]
+        lengths = workloads.draw_lengths(w, np.random.default_rng(w.index))
+        got = thd.preferred_fwd_tiles(seqlens=lengths, cp=w.cp, rank=w.rank, hq=w.hq, hkv=w.hkv,
+                                      d_qk=w.d_qk, d_v=w.d_v, concurrency32=conc)
+        assert got[1] == bn, name
+    with pytest.raises(thd.ThdError) as err:
+        thd.preferred_fwd_tiles(seqlens=[512], cp=1, rank=0, hq=8, hkv=8, d_qk=128, d_v=128,
+                                concurrency32=-1)
+    assert err.value.status == "THD_EINVAL"
+
+
 def test_short_tile_metadata_is_refused_where_it_has_no_kernel():
     """Metadata with 32-key tiles serves the forward for d_qk <= 128 only: the
     backward and the d_qk = 192 forward refuse it before any device check."""
