@@ -273,10 +273,14 @@ std::unique_ptr<Plan> build_plan(const int32_t* seqlens, int32_t n_docs, int32_t
   // that see them (their query tiles' rows), most first, stable.
   {
     const int64_t n_kv = int64_t(p.kvtiles.size() / 8);
+    const int64_t n_q = int64_t(p.tiles.size() / 8);
+    std::vector<int64_t> rows_before(size_t(n_q) + 1, 0);   // prefix sums of tile rows
+    for (int64_t t = 0; t < n_q; ++t)
+      rows_before[size_t(t) + 1] = rows_before[size_t(t)] + p.tiles[size_t(t) * 8 + 2];
     std::vector<int64_t> seen(size_t(n_kv), 0);
     for (int64_t j = 0; j < n_kv; ++j)
-      for (int32_t t = p.kvtiles[size_t(j) * 8 + 3]; t < p.kvtiles[size_t(j) * 8 + 4]; ++t)
-        seen[size_t(j)] += p.tiles[size_t(t) * 8 + 2];
+      seen[size_t(j)] = rows_before[size_t(p.kvtiles[size_t(j) * 8 + 4])] -
+                        rows_before[size_t(p.kvtiles[size_t(j) * 8 + 3])];
     p.kv_order.resize(size_t(n_kv));
     std::iota(p.kv_order.begin(), p.kv_order.end(), 0);
     std::stable_sort(p.kv_order.begin(), p.kv_order.end(),
