@@ -126,3 +126,63 @@ def test_padded_shard_passes_match_oracle(case):
     assert np.all(np.isposinf(got_lse[pad]))
     assert_close(got_o[~pad], want_o[~pad], "O")
     assert_close(got_lse[~pad], want_lse[~pad], "LSE", max_abs=LSE_ABS, mean_abs=LSE_ABS)
+
+
+RANDOM_HEADS = [(8, 8, 64, 64), (16, 4, 128, 128), (12, 4, 128, 128), (8, 8, 192, 128),
+                (64, 8, 128, 128), (32, 1, 128, 128)]
+
+
+@pytest.mark.parametrize("case", range(24))
+def test_random_padded_cases(case):
+    """Seeded random real lengths (any size, padded to multiples of 2cp),
+    context-parallel sizes, ranks and head layouts: the forward on the plain
+    and packed plans, shard by shard, and the backward on both D paths, every
+    element against the oracle, pad rows exactly O = 0 and LSE = +inf."""
+    rng = np.random.default_rng(20000 + case)
+    cp = int(rng.choice([1, 2, 3, 4, 8]))
+    rank = int(rng.integers(0, cp))
+    hq, hkv, dqk, dv = RANDOM_HEADS[case % len(RANDOM_HEADS)]
+    real = [int(x) for x in rng.integers(1, 300, size=int(rng.integers(1, 6)))]
+    print(f"[pad random] case={case} cp={cp} rank={rank} heads={hq}/{hkv} d={dqk} real={real}",
+          flush=True)
+    b = _batch((20000 + case, real, cp, rank, hq, hkv, dqk, dv), backward=True)
+    dev = device()
+    q, k, v, do = (t.to(dev) for t in (b.q, b.k, b.v, b.do))
+    want_o, want_lse = oatt.attn_fwd64_padded(to64(b.q), to64(b.k), to64(b.v), real, cp, rank)
+    pad = opart.pad_rows(real, cp, rank)
+
+    def check(o, lse, what):
+        got_o, got_lse = to64(o), lse.cpu().double().numpy()
+        assert np.all(got_o[pad] == 0.0), what
+        assert np.all(np.isposinf(got_lse[pad])), what
+        assert_close(got_o[~pad], want_o[~pad], what + " O")
+        assert_close(got_lse[~pad], want_lse[~pad], what + " LSE", max_abs=LSE_ABS,
+                     mean_abs=LSE_ABS)
+
+    for packed in (False, True):
+        o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=real, cp=cp, rank=rank, padded=True,
+                              packed=packed)
+        torch.cuda.synchronize()
+        check(o, lse, f"packed={packed}")
+    bt, _ = thd.preferred_tiles(hq=hq, hkv=hkv, d_qk=dqk, d_v=dv)
+    order = [rank] + [s for s in range(cp) if s != rank]
+    state = None
+    for i, s in enumerate(order):
+        meta = thd.build_pass_metadata(seqlens=real, cp=cp, rank=rank, block_t=bt, block_n=64,
+                                       shards=[s], device=0, padded=True)
+        if state is None:
+            state = thd.pass_state(meta=meta, hq=hq, hkv=hkv, d_v=dv, device=dev)
+        res = thd.attn_fwd_pass(q=q, k=k, v=v, meta=meta, state=state, first=i == 0,
+                                last=i == len(order) - 1)
+    torch.cuda.synchronize()
+    check(*res, "shard by shard")
+    want = oatt.attn_bwd64_padded(to64(b.q), to64(b.k), to64(b.v), to64(b.do), real, cp, rank)
+    for exact in (False, True):
+        o32 = torch.empty((q.shape[0], hq, dv), dtype=torch.float32, device=dev) if exact else None
+        o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=real, cp=cp, rank=rank, padded=True,
+                              out_f32=o32)
+        got = thd.attn_bwd(q=q, k=k, v=v, lse=lse, d_o=do, seqlens=real, cp=cp, rank=rank,
+                           o_f32=o32, padded=True)
+        torch.cuda.synchronize()
+        for name, g, e in zip(("dQ", "dK", "dV"), got, want):
+            assert_close(g.cpu().double().numpy(), e, f"{name} exact={exact}")
