@@ -106,6 +106,16 @@ def bf16_normal(rng: np.random.Generator, shape, device="cpu"):
     return torch.from_numpy(x).to(torch.bfloat16).to(device)
 
 
+def device_normal(seed: int, shape, device):
+    """bf16 standard normal drawn on the device by torch's generator seeded with
+    ``seed``: for batches too large to draw on the host."""
+    import torch
+
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    return torch.randn(shape, generator=gen, device=device, dtype=torch.bfloat16)
+
+
 @dataclasses.dataclass
 class Batch:
     workload: Workload
