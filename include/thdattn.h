@@ -28,6 +28,7 @@
  *   dq   fp32 [T_local, Hq,  d_qk]      backward outputs; dk/dv are this
  *   dk   fp32 [T,       Hkv, d_qk]      rank's partial sums in the gathered
  *   dv   fp32 [T,       Hkv, d_v ]      layout, exact zeros for unseen keys
+ *                                       (bf16 from thd_attn_bwd_bf16kv)
  *
  * Conventions for every entry point:
  *   - return 0 (THD_OK) or a negative thd_status; nothing aborts or throws
@@ -426,6 +427,21 @@ int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void*
                  float* dq, float* dk, float* dv,
                  int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v, float softmax_scale,
                  void* workspace, int64_t workspace_bytes, void* hip_stream);
+
+/* thd_attn_bwd with this rank's partial dk and dv written in bf16: the same
+ * fp32 results rounded to nearest even, in the same layouts, so that the
+ * reduce-scatter which sums the ranks' partials ("[Optim] FlashMask-4 Overlap
+ * support part 1 (NVSHMEM backend) - #166", feature list: reduce-scatter
+ * overlapped with the backward) moves half the bytes. Each partial then
+ * carries a rounding error of up to 2^-9 of its magnitude into that sum. dq
+ * stays fp32 (it never leaves the rank). dk: bf16 [T, Hkv, d_qk], dv: bf16
+ * [T, Hkv, d_v], 16-byte aligned; every other argument, the workspace and the
+ * errors as thd_attn_bwd. */
+int thd_attn_bwd_bf16kv(const thd_meta* meta, const void* q, const void* k, const void* v,
+                        const float* lse, const float* o_f32, const void* d_o,
+                        float* dq, void* dk, void* dv,
+                        int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v, float softmax_scale,
+                        void* workspace, int64_t workspace_bytes, void* hip_stream);
 
 #ifdef __cplusplus
 }

@@ -101,6 +101,8 @@ def _load():
         "thd_attn_bwd_workspace": (ctypes.c_int, [p, i32, pi64]),
         "thd_attn_bwd": (ctypes.c_int, [p, p, p, p, p, p, p, p, p, p, i32, i32, i32, i32,
                                         ctypes.c_float, p, i64, p]),
+        "thd_attn_bwd_bf16kv": (ctypes.c_int, [p, p, p, p, p, p, p, p, p, p, i32, i32, i32,
+                                               i32, ctypes.c_float, p, i64, p]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -117,7 +119,7 @@ EXPORTS = ("thd_last_error", "thd_plan_partition", "thd_build_metadata", "thd_pa
            "thd_attn_fwd_workspace", "thd_attn_fwd", "thd_attn_fwd_noalloc",
            "thd_build_pass_metadata", "thd_build_pass_metadata_padded",
            "thd_attn_fwd_pass_state_bytes", "thd_attn_fwd_pass",
-           "thd_attn_bwd_workspace", "thd_attn_bwd")
+           "thd_attn_bwd_workspace", "thd_attn_bwd", "thd_attn_bwd_bf16kv")
 PASS_FIRST = 1
 PASS_LAST = 2
 
@@ -518,9 +520,11 @@ def attn_fwd_noalloc(*, q, k, v, out, lse, meta: Meta, out_f32=None, softmax_sca
 
 def attn_bwd(*, q, k, v, lse, d_o, seqlens, cp: int, rank: int, softmax_scale=None,
              o_f32=None, stream=None, meta: Meta | None = None, workspace=None,
-             padded: bool = False):
-    """Backward for one rank. Returns (dq fp32, dk fp32, dv fp32); dk/dv are
-    this rank's partial sums in the gathered layout (zeros for unseen keys).
+             padded: bool = False, dkdv_dtype=None):
+    """Backward for one rank. Returns (dq fp32, dk, dv); dk/dv are this rank's
+    partial sums in the gathered layout (zeros for unseen keys), fp32, or bf16
+    (the fp32 results rounded to nearest even; thd_attn_bwd_bf16kv) when
+    dkdv_dtype is torch.bfloat16.
     lse is the forward's. o_f32 (optional) is the forward's fp32 O from
     attn_fwd(out_f32=...): D then comes from it instead of a pass over the keys.
     workspace (optional): a device tensor of at least the bytes
@@ -554,13 +558,16 @@ def attn_bwd(*, q, k, v, lse, d_o, seqlens, cp: int, rank: int, softmax_scale=No
     ws_bytes = workspace.numel() * workspace.element_size()
     if ws_bytes < need.value:
         raise ThdError(-1, f"workspace has {ws_bytes} bytes, needs {need.value}")
+    if dkdv_dtype not in (None, torch.float32, torch.bfloat16):
+        raise ThdError(-1, f"dkdv_dtype must be torch.float32 or torch.bfloat16, not {dkdv_dtype}")
+    kv_dtype = torch.float32 if dkdv_dtype is None else dkdv_dtype
     dq = torch.empty(q.shape, dtype=torch.float32, device=dev)
-    dk = torch.empty(k.shape, dtype=torch.float32, device=dev)
-    dv = torch.empty(v.shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(k.shape, dtype=kv_dtype, device=dev)
+    dv = torch.empty(v.shape, dtype=kv_dtype, device=dev)
     scale = 0.0 if softmax_scale is None else float(softmax_scale)
-    _check(_lib.thd_attn_bwd(meta.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                             lse.data_ptr(), None if o_f32 is None else o_f32.data_ptr(),
-                             d_o.data_ptr(), dq.data_ptr(), dk.data_ptr(),
-                             dv.data_ptr(), hq, hkv, d_qk, d_v, scale, workspace.data_ptr(),
-                             ws_bytes, _stream_handle(stream, dev)))
+    fn = _lib.thd_attn_bwd_bf16kv if kv_dtype == torch.bfloat16 else _lib.thd_attn_bwd
+    _check(fn(meta.handle, q.data_ptr(), k.data_ptr(), v.data_ptr(), lse.data_ptr(),
+              None if o_f32 is None else o_f32.data_ptr(), d_o.data_ptr(), dq.data_ptr(),
+              dk.data_ptr(), dv.data_ptr(), hq, hkv, d_qk, d_v, scale, workspace.data_ptr(),
+              ws_bytes, _stream_handle(stream, dev)))
     return dq, dk, dv

@@ -189,8 +189,8 @@ struct BwdParams {
   const float* o_f32;   // optional exact O (fp32); D = rowsum(dO * O) from it when given
   const void* d_o;
   float* dq;
-  float* dk;
-  float* dv;
+  void* dk;           // fp32, or bf16 when kv_bf16
+  void* dv;
   float* delta;       // workspace: D [T_local, Hq]
   float* lse2;        // workspace: lse * log2(e) [T_local, Hq]
   const int32_t* tiles;
@@ -199,6 +199,7 @@ struct BwdParams {
   const int32_t* kv_order;   // dK/dV workgroup b takes key tile kv_order[b / hkv]
   const int32_t* kv_row;
   int32_t n_tiles, n_kvtiles, hq, hkv, group, block_t;
+  int32_t kv_bf16;    // dk, dv stored as bf16 (round to nearest even) instead of fp32
   int64_t total, local;
   float scale;        // softmax_scale
   float scale_log2;   // softmax_scale * log2(e)

@@ -739,11 +739,17 @@ int thd_attn_bwd_workspace(const thd_meta* meta, int32_t hq, int64_t* bytes) {
   });
 }
 
-int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void* v,
-                 const float* lse, const float* o_f32, const void* d_o, float* dq, float* dk,
-                 float* dv, int32_t hq,
-                 int32_t hkv, int32_t d_qk, int32_t d_v, float softmax_scale, void* workspace,
-                 int64_t workspace_bytes, void* hip_stream) {
+}  // extern "C"
+
+namespace thd {
+namespace {
+
+// Both backward entry points: dk and dv in fp32, or in bf16 (kv_bf16).
+int attn_bwd_impl(const thd_meta* meta, const void* q, const void* k, const void* v,
+                  const float* lse, const float* o_f32, const void* d_o, float* dq, void* dk,
+                  void* dv, int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
+                  float softmax_scale, void* workspace, int64_t workspace_bytes,
+                  void* hip_stream, bool kv_bf16) {
   return guarded([&] {
     const MetaEntry& e = entry_of(meta);
     const Plan& p = *e.plan;
@@ -803,10 +809,34 @@ int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void*
     bp.block_t = p.block_t;
     bp.total = p.total;
     bp.local = p.local;
+    bp.kv_bf16 = kv_bf16 ? 1 : 0;
     bp.scale = softmax_scale;
     bp.scale_log2 = softmax_scale * 1.4426950408889634f;
     check_hip(hipError_t(launch_bwd(bp, d_qk, d_v, hip_stream)), "backward launch");
   });
+}
+
+}  // namespace
+}  // namespace thd
+
+extern "C" {
+
+int thd_attn_bwd(const thd_meta* meta, const void* q, const void* k, const void* v,
+                 const float* lse, const float* o_f32, const void* d_o, float* dq, float* dk,
+                 float* dv, int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
+                 float softmax_scale, void* workspace, int64_t workspace_bytes,
+                 void* hip_stream) {
+  return attn_bwd_impl(meta, q, k, v, lse, o_f32, d_o, dq, dk, dv, hq, hkv, d_qk, d_v,
+                       softmax_scale, workspace, workspace_bytes, hip_stream, false);
+}
+
+int thd_attn_bwd_bf16kv(const thd_meta* meta, const void* q, const void* k, const void* v,
+                        const float* lse, const float* o_f32, const void* d_o, float* dq,
+                        void* dk, void* dv, int32_t hq, int32_t hkv, int32_t d_qk, int32_t d_v,
+                        float softmax_scale, void* workspace, int64_t workspace_bytes,
+                        void* hip_stream) {
+  return attn_bwd_impl(meta, q, k, v, lse, o_f32, d_o, dq, dk, dv, hq, hkv, d_qk, d_v,
+                       softmax_scale, workspace, workspace_bytes, hip_stream, true);
 }
 
 }  // extern "C"

@@ -816,14 +816,27 @@ __global__ __launch_bounds__(kDkvWaves * 64, DQK > 128 ? 2 : 3) void thd_bwd_dkd
     const int kr = wave * kDkvKeysPerWave + 4 * grp + i;
     grows[i] = kr < nk ? p.kv_row[ks + kr] : -1;
   }
+  // bf16 output: the same fp32 values, rounded to nearest even.
+  const bool out_bf16 = p.kv_bf16 != 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (grows[i] < 0) continue;
     const size_t grow = size_t(grows[i]) * hkv + kvh;
+    if (out_bf16) {
+      __bf16* dk16 = static_cast<__bf16*>(p.dk) + grow * DQK + lr;
+      __bf16* dv16 = static_cast<__bf16*>(p.dv) + grow * DV + lr;
 #pragma unroll
-    for (int nt = 0; nt < S::KT; ++nt) p.dk[grow * DQK + 16 * nt + lr] = dk[nt][i] * p.scale;
+      for (int nt = 0; nt < S::KT; ++nt) dk16[16 * nt] = static_cast<__bf16>(dk[nt][i] * p.scale);
 #pragma unroll
-    for (int nt = 0; nt < S::VT; ++nt) p.dv[grow * DV + 16 * nt + lr] = dv[nt][i];
+      for (int nt = 0; nt < S::VT; ++nt) dv16[16 * nt] = static_cast<__bf16>(dv[nt][i]);
+    } else {
+      float* dk32 = static_cast<float*>(p.dk) + grow * DQK + lr;
+      float* dv32 = static_cast<float*>(p.dv) + grow * DV + lr;
+#pragma unroll
+      for (int nt = 0; nt < S::KT; ++nt) dk32[16 * nt] = dk[nt][i] * p.scale;
+#pragma unroll
+      for (int nt = 0; nt < S::VT; ++nt) dv32[16 * nt] = dv[nt][i];
+    }
   }
 }
 

@@ -125,3 +125,40 @@ def test_backward_gradient_identities_on_gpu():
         got = dv[:, hk].double().sum(0).cpu()
         assert torch.allclose(got, want, atol=5e-2, rtol=1e-3)
         assert dk[:, hk].double().sum(0).abs().max().item() < 5e-2
+
+
+BF16_KV = [SMALL[1], SMALL[4], SMALL[5], SMALL[6]]
+
+
+@pytest.mark.parametrize("exact_o", [False, True], ids=["D_from_scores", "D_from_o32"])
+@pytest.mark.parametrize("case", BF16_KV + ["fwdbwd"], ids=lambda c: c if isinstance(c, str) else f"seed{c[0]}")
+def test_backward_bf16_dkdv_are_the_fp32_results_rounded(case, exact_o):
+    """thd_attn_bwd_bf16kv: dk and dv are the fp32 path's values rounded to
+    nearest even, bit for bit, and dq is the fp32 path's, bit for bit; against
+    the oracle they stay within the bound plus one bf16 rounding."""
+    if case == "fwdbwd":
+        w = workloads.BY_NAME[case]
+        b = workloads.make_batch(w)
+    else:
+        seed, lengths, cp, rank, hq, hkv, dqk, dv = case
+        b = workloads.small_case(seed, lengths, cp, hq, hkv, dqk, dv, backward=True, rank=rank)
+        w = b.workload
+    dev = device()
+    q, k, v, do = (t.to(dev) for t in (b.q, b.k, b.v, b.do))
+    print(f"[bwd bf16 dk/dv] case={w.name} cp={w.cp} rank={w.rank} hq={w.hq} hkv={w.hkv} "
+          f"dqk={w.d_qk} exact_o={exact_o}", flush=True)
+    o32 = torch.empty((q.shape[0], w.hq, w.d_v), dtype=torch.float32, device=dev) if exact_o else None
+    o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=b.lengths, cp=w.cp, rank=w.rank, out_f32=o32)
+    args = dict(q=q, k=k, v=v, lse=lse, d_o=do, seqlens=b.lengths, cp=w.cp, rank=w.rank, o_f32=o32)
+    dq32, dk32, dv32 = thd.attn_bwd(**args)
+    dq, dk, dv = thd.attn_bwd(**args, dkdv_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert dk.dtype == torch.bfloat16 and dv.dtype == torch.bfloat16 and dq.dtype == torch.float32
+    assert torch.equal(dq, dq32)
+    assert torch.equal(dk, dk32.to(torch.bfloat16)) and torch.equal(dv, dv32.to(torch.bfloat16))
+    want = oatt.attn_bwd64(to64(b.q), to64(b.k), to64(b.v), to64(b.do), b.lengths, w.cp, w.rank)
+    for name, g, e in zip(("dK", "dV"), (dk, dv), want[1:]):
+        err = np.abs(to64(g) - e)
+        print(f"[bwd bf16 dk/dv] {name} max-abs {err.max():.3g} (|ref| max {np.abs(e).max():.3g})",
+              flush=True)
+        assert np.all(err <= 2e-2 + 2.0 ** -8 * np.abs(e)), name

@@ -209,6 +209,29 @@ def test_short_tile_metadata_is_refused_where_it_has_no_kernel():
     assert lib.thd_fwd_concurrency(0, 0, 64, ctypes.byref(c)) == -1
 
 
+def test_bf16_dkdv_backward_checks_its_arguments_as_the_fp32_one():
+    """thd_attn_bwd_bf16kv shares thd_attn_bwd's checks: each bad argument
+    gets the same status from both, before any device work."""
+    m = thd.build_metadata(seqlens=[256], cp=1, rank=0, block_t=32, block_n=64)
+    m32 = thd.build_metadata(seqlens=[256], cp=1, rank=0, block_t=32, block_n=32)
+    buf = ctypes.create_string_buffer(1 << 16)
+    ptr = (ctypes.addressof(buf) + 15) // 16 * 16
+    lib = thd._lib
+    cases = [
+        ((m.handle, ptr, ptr, ptr, ptr, None, ptr, ptr, ptr, ptr), (32, 8, 96, 96, 0.1), -8),
+        ((m.handle, ptr, ptr, ptr, ptr, None, ptr, ptr, ptr, ptr), (32, 8, 128, 128, -1.0), -1),
+        ((m.handle, ptr, ptr, ptr, ptr, None, ptr, ptr, ptr, ptr), (30, 8, 128, 128, 0.1), -1),
+        ((m32.handle, ptr, ptr, ptr, ptr, None, ptr, ptr, ptr, ptr), (32, 8, 128, 128, 0.1), -5),
+        ((m.handle, ptr, ptr, ptr, ptr, None, ptr, ptr, ptr + 2, ptr), (32, 8, 128, 128, 0.1), -4),
+        ((m.handle, ptr, ptr, ptr, ptr, None, ptr, ptr, ptr, None), (32, 8, 128, 128, 0.1), -1),
+        ((m.handle, ptr, ptr, ptr, ptr, None, ptr, ptr, ptr, ptr), (32, 8, 128, 128, 0.1), -5),
+    ]
+    for ptrs, dims, status in cases:
+        for fn in (lib.thd_attn_bwd, lib.thd_attn_bwd_bf16kv):
+            assert fn(*ptrs, *dims, ptr, 1 << 16, None) == status, (fn.__name__, dims, status)
+    assert b"device" in lib.thd_last_error()   # host-only metadata cannot launch
+
+
 @pytest.mark.parametrize("kwargs,status", [
     (dict(seqlens=[6, 8], cp=2, rank=0), "THD_ENOTDIV"),
     (dict(seqlens=[8], cp=2, rank=2), "THD_ERANGE"),
