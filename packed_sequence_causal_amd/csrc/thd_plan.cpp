@@ -39,7 +39,8 @@ int64_t validate_partition(const int32_t* seqlens, int32_t n_docs, int32_t cp, i
   if (seqlens == nullptr) fail(THD_EINVAL, "seqlens is NULL");
   if (n_docs < 1) fail(THD_EINVAL, "n_docs must be >= 1");
   if (cp < 1) fail(THD_ERANGE, "cp must be >= 1");
-  if (rank < 0 || rank >= cp) fail(THD_ERANGE, "rank must be in [0, cp)");
+  if (rank < 0 || rank >= cp)
+    fail(THD_ERANGE, "rank " + std::to_string(rank) + " outside [0, " + std::to_string(cp) + ")");
   int64_t total = 0;
   for (int32_t i = 0; i < n_docs; ++i) {
     const int64_t len = seqlens[i];
