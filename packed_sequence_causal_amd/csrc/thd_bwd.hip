@@ -37,7 +37,9 @@
 //      each lane with one key and 8 rows, which is the A-operand layout of P^T
 //      and dS^T, so dV += P^T dO and dK += dS^T Q take their B operands from
 //      the row-major dO and Q blocks with transpose reads. Tiles no local
-//      query sees write zeros.
+//      query sees write zeros. dK and dV are stored in fp32, or rounded to
+//      bf16 (nearest even) when the caller asks for half the bytes in the
+//      reduce-scatter.
 // Dispatch order: dQ-kernel workgroups take query tiles in the plan's order
 // (most KV tiles first), dK/dV workgroups key tiles by the local query tokens
 // that see them (most first). Each workgroup writes only its own rows, so the
