@@ -5,6 +5,8 @@ over every output; properties that hold at any size are checked besides
 (document-start rows, EOD isolation, causality, determinism, union over
 ranks).
 """
+import functools
+
 import numpy as np
 import pytest
 import torch
@@ -237,6 +239,40 @@ def test_forward_full_size_every_element(w):
         got = o[torch.tensor(starts, device=o.device)].cpu()
         want = b.v[torch.from_numpy(rows_v.astype(np.int64))].repeat_interleave(group, dim=1)
         assert torch.equal(got, want)
+
+
+OTHER_RANKS = [(name, r) for name in ("gqa_mid", "mla", "short")
+               for r in range(workloads.BY_NAME[name].cp) if r != workloads.BY_NAME[name].rank]
+
+
+@functools.lru_cache(maxsize=1)
+def _full_batch(name):
+    """One workload's batch, on the host and on the device, drawn once for all its ranks."""
+    b = workloads.make_batch(workloads.BY_NAME[name])
+    dev = device()
+    return b, (b.q.to(dev), b.k.to(dev), b.v.to(dev)), (to64(b.q), to64(b.k), to64(b.v))
+
+
+@pytest.mark.parametrize("name,rank", OTHER_RANKS, ids=lambda x: str(x))
+def test_forward_full_size_every_rank(name, rank):
+    """The full-size forward workloads at every other rank of their
+    context-parallel group (same batch, that rank's share and plan): every
+    element of O and LSE against the fp64 oracle."""
+    w = workloads.BY_NAME[name]
+    # the batch's Q is drawn for the workload's own rank; any rank's share has
+    # the same shape, and these values stand in for it
+    b, (q, k, v), (q64, k64, v64) = _full_batch(name)
+    meta = thd.device_metadata(seqlens=b.lengths, cp=w.cp, rank=rank, hq=w.hq, hkv=w.hkv,
+                               d_qk=w.d_qk, d_v=w.d_v, device=0, forward=True)
+    info = meta.info()
+    print(f"[fwd rank] {name} rank={rank} block_n={info['block_n']} items={info['n_items']} "
+          f"splits={info['n_splits']}", flush=True)
+    o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=b.lengths, cp=w.cp, rank=rank, meta=meta)
+    torch.cuda.synchronize()
+    want_o, want_lse = oatt.attn_fwd64(q64, k64, v64, b.lengths, w.cp, rank)
+    assert_close(to64(o), want_o, f"{name} rank {rank} O")
+    assert_close(lse.cpu().double().numpy(), want_lse, f"{name} rank {rank} LSE",
+                 max_abs=LSE_ABS, mean_abs=LSE_ABS)
 
 
 def test_forward_tiny_full_compare():
