@@ -114,6 +114,24 @@ def test_backward_fwdbwd_workload_full(exact_o):
     assert torch.equal(dq, dq2) and torch.equal(dk, dk2) and torch.equal(dv, dv2)
 
 
+@pytest.mark.parametrize("rank", [0, 1, 3])
+def test_backward_fwdbwd_workload_other_ranks(rank):
+    """The full training workload at the other ranks of its group (the batch's
+    Q and dO stand in for that rank's share), training path (D from the fp32
+    O): every element of dQ, dK, dV against the oracle, unseen keys zero."""
+    w = workloads.BY_NAME["fwdbwd"]
+    b = workloads.make_batch(w)
+    dq, dk, dv = _run(b, rank=rank, exact_o=True)
+    _check(b, (dq, dk, dv), rank=rank)
+    cu = opart.cu_seqlens(b.lengths)
+    rows = opart.kv_row(b.lengths, w.cp)
+    unseen = np.concatenate([rows[cu[i] + (2 * w.cp - rank) * (int(L) // (2 * w.cp)):cu[i + 1]]
+                             for i, L in enumerate(b.lengths)]).astype(np.int64)
+    if unseen.size:
+        idx = torch.from_numpy(unseen).to(dk.device)
+        assert torch.count_nonzero(dk[idx]).item() == 0 and torch.count_nonzero(dv[idx]).item() == 0
+
+
 def test_backward_gradient_identities_on_gpu():
     lengths, cp, rank, hq, hkv = [96, 480, 192], 4, 1, 16, 4
     b = workloads.small_case(59, lengths, cp, hq, hkv, 128, 128, backward=True, rank=rank)
