@@ -146,10 +146,13 @@ def test_overlapped_delivery_and_grouped_passes(case):
                      mean_abs=LSE_ABS)
 
 
-def test_full_size_gqa_mid_shard_passes():
-    """The GQA-mid workload (T 16384, cp 4, rank 1) shard by shard: every
-    element of O and LSE against the oracle."""
-    w = workloads.BY_NAME["gqa_mid"]
+@pytest.mark.parametrize("name", ["gqa_mid", "mla", "short"])
+def test_full_size_shard_passes(name):
+    """The full-size forward workloads (gqa_mid: cp 4; mla and short: cp 8)
+    shard by shard, the local shard first: every element of O and LSE against
+    the oracle."""
+    w = workloads.BY_NAME[name]
+    print(f"[ag full] {name} cp={w.cp} rank={w.rank}", flush=True)
     b = workloads.make_batch(w)
     dev = device()
     q, k, v = b.q.to(dev), b.k.to(dev), b.v.to(dev)
