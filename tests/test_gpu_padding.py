@@ -186,3 +186,45 @@ def test_random_padded_cases(case):
         torch.cuda.synchronize()
         for name, g, e in zip(("dQ", "dK", "dV"), got, want):
             assert_close(g.cpu().double().numpy(), e, f"{name} exact={exact}")
+
+
+@pytest.mark.parametrize("name", ["gqa_mid", "fwdbwd"])
+def test_padded_full_size(name):
+    """A full-size workload whose documents end anywhere: the workload's own
+    lengths shortened by a seeded 0 .. 2cp-1 tokens each, padded back. Forward
+    (and, for the training workload, the backward from the fp32 O) on every
+    element against the oracle; pad rows and pad keys exact."""
+    w = workloads.BY_NAME[name]
+    b = workloads.make_batch(w)
+    lengths = b.lengths
+    rng = np.random.default_rng(w.index + 700)
+    real = [max(1, int(L) - int(rng.integers(0, 2 * w.cp))) for L in lengths]
+    assert opart.pad_lengths(real, w.cp) == [int(L) for L in lengths]
+    print(f"[pad full] {name} pad tokens={sum(lengths) - sum(real)}", flush=True)
+    dev = device()
+    q, k, v = (t.to(dev) for t in (b.q, b.k, b.v))
+    pad = opart.pad_rows(real, w.cp, w.rank)
+    o32 = torch.empty((q.shape[0], w.hq, w.d_v), dtype=torch.float32, device=dev)
+    o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=real, cp=w.cp, rank=w.rank, padded=True,
+                          out_f32=o32)
+    torch.cuda.synchronize()
+    want_o, want_lse = oatt.attn_fwd64_padded(to64(b.q), to64(b.k), to64(b.v), real, w.cp, w.rank)
+    got_o, got_lse = to64(o), lse.cpu().double().numpy()
+    assert np.all(got_o[pad] == 0.0) and np.all(np.isposinf(got_lse[pad]))
+    real_rows = ~np.isin(np.arange(q.shape[0]), pad)
+    assert_close(got_o[real_rows], want_o[real_rows], f"{name} padded O")
+    assert_close(got_lse[real_rows], want_lse[real_rows], f"{name} padded LSE",
+                 max_abs=LSE_ABS, mean_abs=LSE_ABS)
+    if name != "fwdbwd":
+        return
+    do = b.do.to(dev)
+    dq, dk, dvv = thd.attn_bwd(q=q, k=k, v=v, lse=lse, d_o=do, seqlens=real, cp=w.cp,
+                               rank=w.rank, padded=True, o_f32=o32)
+    torch.cuda.synchronize()
+    want = oatt.attn_bwd64_padded(to64(b.q), to64(b.k), to64(b.v), to64(b.do), real, w.cp, w.rank)
+    got = [t.cpu().double().numpy() for t in (dq, dk, dvv)]
+    pad_keys = _pad_keys(real, w.cp)
+    assert np.all(got[0][pad] == 0.0)
+    assert np.all(got[1][pad_keys] == 0.0) and np.all(got[2][pad_keys] == 0.0)
+    for gname, g, e in zip(("dQ", "dK", "dV"), got, want):
+        assert_close(g, e, f"{name} padded {gname}")
