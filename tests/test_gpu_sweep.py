@@ -30,7 +30,7 @@ def _draw(case):
     rng = np.random.default_rng(9000 + case)
     cp = int(rng.choice([1, 2, 3, 4, 8]))
     rank = int(rng.integers(0, cp))
-    hq, hkv, dqk, dv = HEADS[case % len(HEADS)]     # every layout six times
+    hq, hkv, dqk, dv = HEADS[case % len(HEADS)]     # every layout twelve times
     n = int(rng.integers(1, 7))
     # chunk lengths from 1 token to a few hundred, total at most ~4k tokens
     chunk = rng.choice([1, 2, 3, 8, 17, 40, 64, 100, 255], size=n)
@@ -41,7 +41,7 @@ def _draw(case):
     return cp, rank, hq, hkv, dqk, dv, lengths, concurrency
 
 
-@pytest.mark.parametrize("case", range(48))
+@pytest.mark.parametrize("case", range(96))
 def test_random_shapes(case):
     cp, rank, hq, hkv, dqk, dv, lengths, concurrency = _draw(case)
     print(f"[sweep] case={case} cp={cp} rank={rank} hq={hq} hkv={hkv} dqk={dqk} dv={dv} "
