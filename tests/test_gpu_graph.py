@@ -1,9 +1,10 @@
-"""The forward that allocates nothing, captured in a HIP graph (torch.cuda.graph)
-on an MI355X: replays over inputs rewritten in place, with eager calls on other
-inputs in between (they overwrite the library's static array of partial
-results), must equal the eager forward bit for bit on every replay, and the
-oracle within the bound. A split plan puts both the forward and the combine
-kernel into the graph."""
+"""HIP graphs (torch.cuda.graph) on an MI355X. The forward that allocates
+nothing, captured alone: replays over inputs rewritten in place, with eager
+calls on other inputs in between (they overwrite the library's static array of
+partial results), must equal the eager forward bit for bit on every replay, and
+the oracle within the bound; a split plan puts both the forward and the combine
+kernel into the graph. A training step (forward with the fp32 O, backward)
+captured whole: every replay equals the eager step bit for bit."""
 import pytest
 import torch
 
@@ -69,3 +70,45 @@ def test_noalloc_forward_replays_in_a_graph(case):
             assert_close(to64(out), o64, "O")
             assert_close(lse.cpu().double().numpy(), lse64, "LSE", max_abs=LSE_ABS,
                          mean_abs=LSE_ABS)
+
+
+def test_training_step_replays_in_a_graph():
+    """Forward (with the fp32 O) and backward captured together; their outputs
+    and workspaces come from the graph's memory pool. Every replay over
+    rewritten inputs equals the eager step bit for bit."""
+    seed, lengths, cp, rank, hq, hkv, dqk, dv = 9511, [1000, 72, 600], 4, 2, 32, 8, 128, 128
+    dev = device()
+    b = workloads.small_case(seed, lengths, cp, hq, hkv, dqk, dv, backward=True, rank=rank)
+    q, k, v, do = (t.to(dev) for t in (b.q, b.k, b.v, b.do))
+    meta = thd.device_metadata(seqlens=b.lengths, cp=cp, rank=rank, hq=hq, hkv=hkv, d_qk=dqk,
+                               d_v=dv, device=0)
+
+    def step():
+        o32 = torch.empty((q.shape[0], hq, dv), dtype=torch.float32, device=dev)
+        o, lse = thd.attn_fwd(q=q, k=k, v=v, seqlens=b.lengths, cp=cp, rank=rank, out_f32=o32,
+                              meta=meta)
+        return (o, lse) + tuple(thd.attn_bwd(q=q, k=k, v=v, lse=lse, d_o=do, seqlens=b.lengths,
+                                             cp=cp, rank=rank, o_f32=o32, meta=meta))
+
+    side = torch.cuda.Stream(device=dev)
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        captured = step()
+    for rep in range(REPLAYS):
+        fresh = workloads.small_case(seed + 100 + rep, lengths, cp, hq, hkv, dqk, dv,
+                                     backward=True, rank=rank)
+        for dst, src in zip((q, k, v, do), (fresh.q, fresh.k, fresh.v, fresh.do)):
+            dst.copy_(src.to(dev))
+        torch.cuda.synchronize()
+        print(f"[graph] training step replay {rep}", flush=True)
+        graph.replay()
+        torch.cuda.synchronize()
+        want = step()
+        torch.cuda.synchronize()
+        for name, g, e in zip(("O", "LSE", "dQ", "dK", "dV"), captured, want):
+            assert torch.equal(g, e), (rep, name)
